@@ -1,0 +1,133 @@
+// Launch glue of libdpp: argument checks, work-list upload, kernel launches.
+//
+// Nothing here allocates or frees device memory or synchronises a stream. The only HIP
+// allocation is the plan's pinned host copy of its work list (made on first use, so that
+// planning itself stays HIP-free).
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+#include "plan.h"
+
+using namespace dpp;
+
+namespace {
+
+dpp_status hip_fail(hipError_t e, const char* what) {
+  return fail(DPP_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" void dpp_plan_destroy(dpp_plan* plan) {
+  if (!plan) return;
+  if (plan->pinned) (void)hipHostFree(plan->pinned);
+  delete plan;
+}
+
+extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows,
+                              const void* k_pool, const void* v_pool, int64_t num_pages,
+                              const int32_t* kv_indices, void* o, float* lse, void* workspace,
+                              size_t workspace_bytes, void* stream_ptr) {
+  if (!plan) return fail(DPP_ERR_INVALID, "dpp_run: null plan");
+  if (q_rows != plan->total_q_rows)
+    return fail(DPP_ERR_SHAPE, "q has " + std::to_string(q_rows) + " rows but qo_indptr[-1] is " +
+                                   std::to_string(plan->total_q_rows));
+  if (num_pages < 0) return fail(DPP_ERR_INVALID, "dpp_run: negative num_pages");
+  if (!workspace) return fail(DPP_ERR_WORKSPACE, "dpp_run: null workspace");
+  if (!aligned(workspace, 256)) return fail(DPP_ERR_WORKSPACE, "dpp_run: workspace not 256-byte aligned");
+  if (workspace_bytes < plan->workspace_bytes)
+    return fail(DPP_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                       " B, the plan needs " + std::to_string(plan->workspace_bytes) + " B");
+  if (plan->total_q_rows > 0 && (!q || !o || !lse))
+    return fail(DPP_ERR_INVALID, "dpp_run: null q, o or lse");
+  if (plan->num_items > 0 && (!k_pool || !v_pool || !kv_indices))
+    return fail(DPP_ERR_INVALID, "dpp_run: null k_pool, v_pool or kv_indices");
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(lse, 4) || !aligned(kv_indices, 4))
+    return fail(DPP_ERR_INVALID, "dpp_run: q/o/k_pool/v_pool must be 16-byte aligned");
+  hipStream_t stream = (hipStream_t)stream_ptr;
+  if (plan->num_items == 0) return DPP_OK;
+
+  const size_t hbytes = plan->header.size() * sizeof(int32_t);
+  {
+    std::lock_guard<std::mutex> lock(plan->pinned_mu);
+    if (!plan->pinned) {
+      void* p = nullptr;
+      hipError_t e = hipHostMalloc(&p, hbytes, hipHostMallocDefault);
+      if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work list)");
+      std::memcpy(p, plan->header.data(), hbytes);
+      plan->pinned = p;
+    }
+  }
+  hipError_t e = hipMemcpyAsync(workspace, plan->pinned, hbytes, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+
+  char* ws = (char*)workspace;
+  PrefillArgs a{};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.kv_indices = kv_indices;
+  a.o = o;
+  a.lse = lse;
+  a.header = (const int32_t*)workspace;
+  a.part_o = (float*)(ws + plan->partial_o_offset);
+  a.part_lse2 = (float*)(ws + plan->partial_lse_offset);
+  a.num_pages = num_pages;
+  a.num_qo_heads = plan->cfg.num_qo_heads;
+  a.num_kv_heads = plan->cfg.num_kv_heads;
+  a.group = plan->group;
+  a.page_size = plan->cfg.page_size;
+  a.page_slots = plan->page_slots;
+  a.scale_log2 = plan->scale_log2;
+  a.k_scale = plan->cfg.k_scale;
+  a.v_scale = plan->cfg.v_scale;
+
+  MergeArgs m{};
+  m.header = a.header;
+  m.part_o = a.part_o;
+  m.part_lse2 = a.part_lse2;
+  m.o = o;
+  m.lse = lse;
+  m.num_qo_heads = plan->cfg.num_qo_heads;
+  m.group = plan->group;
+
+  const int passes = (int)plan->item_pass.size() - 1;
+  for (int p = 0; p < passes; ++p) {
+    a.item_begin = plan->item_pass[(size_t)p];
+    a.num_items = plan->item_pass[(size_t)p + 1] - a.item_begin;
+    if (a.num_items > 0) {
+      e = launch_prefill(a, plan->cfg.head_dim, plan->cfg.kv_dtype, stream);
+      if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    }
+    m.merge_begin = plan->merge_pass[(size_t)p];
+    m.num_merges = plan->merge_pass[(size_t)p + 1] - m.merge_begin;
+    if (m.num_merges > 0) {
+      e = launch_merge(m, plan->cfg.head_dim, plan->cfg.num_kv_heads, stream);
+      if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+  }
+  return DPP_OK;
+}
+
+extern "C" dpp_status dpp_merge_states(const float* o_partial, const float* lse_partial,
+                                       int64_t num_rows, int32_t num_splits, int32_t num_heads,
+                                       int32_t head_dim, void* o, float* lse, void* stream_ptr) {
+  if (num_rows < 0 || num_heads <= 0 || num_splits < 1 || num_splits > 1024)
+    return fail(DPP_ERR_INVALID, "dpp_merge_states: need num_rows >= 0, num_heads >= 1, 1 <= num_splits <= 1024");
+  if (head_dim <= 0 || head_dim % 4 != 0 || head_dim > 1024)
+    return fail(DPP_ERR_UNSUPPORTED, "dpp_merge_states: head_dim must be a multiple of 4 in [4, 1024]");
+  if (num_rows == 0) return DPP_OK;
+  if (!o_partial || !lse_partial || !o || !lse) return fail(DPP_ERR_INVALID, "dpp_merge_states: null pointer");
+  if (!aligned(o_partial, 16) || !aligned(o, 8) || !aligned(lse_partial, 4) || !aligned(lse, 4))
+    return fail(DPP_ERR_INVALID, "dpp_merge_states: o_partial must be 16-byte and o 8-byte aligned");
+  MergeDenseArgs a{o_partial, lse_partial, o, lse, num_rows, num_splits, num_heads, head_dim};
+  hipError_t e = launch_merge_dense(a, (hipStream_t)stream_ptr);
+  if (e != hipSuccess) return hip_fail(e, "merge launch");
+  return DPP_OK;
+}

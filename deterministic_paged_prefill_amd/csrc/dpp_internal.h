@@ -1,0 +1,137 @@
+// Internal constants and work-list record formats of libdpp (not part of the C ABI).
+//
+// Fixed arithmetic constants. Together with the MFMA instruction shapes and the softmax code
+// in prefill.hip, these decide every bit of a row. They depend on nothing about the batch;
+// this is how a prefix-cache hit reproduces the full prefill (the sglang PR #46351 page,
+// "Root cause", shows FlashInfer losing that property by sizing its q tile from the batch's
+// average query length).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+
+#if defined(__HIPCC__)
+#define DPP_HOST_DEVICE __host__ __device__
+#else
+#define DPP_HOST_DEVICE
+#endif
+
+namespace dpp {
+
+// Packed query rows per tile. A packed row is (token, q head within the kv head's group);
+// row R of a request covers token R / group and q head kv_head * group + R % group.
+constexpr int kBlockM = 128;
+// Keys per KV tile. Tiles start at absolute key positions 0, 64, 128, ...
+constexpr int kBlockN = 64;
+// Fixed KV split length (the model-serving-minefield issue #73 correction comment,
+// "What the flag actually does", item 2). Splits start at absolute positions 0, 4096, ...
+constexpr int kSplitTokens = 4096;
+constexpr int kTilesPerSplit = kSplitTokens / kBlockN;
+static_assert(kSplitTokens % kBlockN == 0, "splits must be whole KV tiles");
+
+constexpr int kThreads = 256;  // four wave64 per workgroup, 32 packed rows each
+constexpr int kWaves = kThreads / 64;
+static_assert(kWaves * 32 == kBlockM, "each wave owns 32 packed rows");
+
+constexpr uint32_t kHeaderMagic = 0x44505031u;  // "DPP1"
+constexpr int kHeaderWords = 16;                // fixed preamble (see HeaderPreamble)
+
+// ---- work-list records (int32 words, uploaded to the head of the workspace) ----
+
+// Per request: where its query rows start in q, how many, where its page list starts in
+// kv_indices, and how many KV tokens it has.
+struct RequestDesc {
+  int32_t q_start;
+  int32_t qo_len;
+  int32_t page_start;
+  int32_t kv_len;
+};
+
+// One (q tile, KV split) unit of the prefill kernel, for every kv head (grid.y).
+struct PrefillItem {
+  int32_t request;
+  int32_t row_start;     // first packed row of the tile (multiple of kBlockM)
+  int32_t split;         // split index s; keys [s*4096, (s+1)*4096)
+  int32_t tile_splits;   // splits the tile's last row needs (S_t)
+  int32_t kv_tile_begin; // first KV tile (absolute, units of kBlockN)
+  int32_t kv_tile_end;   // one past the last KV tile this item visits
+  int32_t slot_base;     // first partial slot of the tile in this pass, -1 if S_t == 1
+  int32_t pad;
+};
+
+// One q tile whose rows span several splits: merge its partials.
+struct MergeItem {
+  int32_t request;
+  int32_t row_start;
+  int32_t tile_splits;
+  int32_t slot_base;
+};
+
+// Partial slot of (kv head c, split s, tile-local row lr) inside a tile's slot block.
+DPP_HOST_DEVICE inline int64_t partial_slot(int32_t slot_base, int32_t tile_splits, int c,
+                                                int s, int lr) {
+  return (int64_t)slot_base + ((int64_t)c * tile_splits + s) * kBlockM + lr;
+}
+
+struct HeaderPreamble {
+  uint32_t magic;
+  int32_t num_requests;
+  int32_t num_items;
+  int32_t num_merges;
+  int32_t request_offset;  // word offsets from the start of the header
+  int32_t item_offset;
+  int32_t merge_offset;
+  int32_t reserved[kHeaderWords - 7];
+};
+static_assert(sizeof(HeaderPreamble) == kHeaderWords * 4, "preamble size");
+
+// ---- kernel launch arguments ----
+
+struct PrefillArgs {
+  const void* q;            // bf16 [rows, Hq, D]
+  const void* k_pool;       // [pages, page_size, Hkv, D] bf16 or e4m3
+  const void* v_pool;
+  const int32_t* kv_indices;
+  void* o;                  // bf16 [rows, Hq, D]
+  float* lse;               // [rows, Hq]
+  const int32_t* header;    // device copy of the work list
+  float* part_o;            // [slots, D]
+  float* part_lse2;         // [slots] (base-2 log-sum-exp of the split)
+  int64_t num_pages;
+  int32_t item_begin;       // first item of this pass
+  int32_t num_items;        // items in this pass
+  int32_t num_qo_heads;
+  int32_t num_kv_heads;
+  int32_t group;
+  int32_t page_size;
+  int32_t page_slots;       // entries of the per-item page-id table in LDS
+  float scale_log2;         // sm_scale * log2(e), rounded once to fp32
+  float k_scale;
+  float v_scale;
+};
+
+struct MergeArgs {
+  const int32_t* header;
+  const float* part_o;
+  const float* part_lse2;
+  void* o;
+  float* lse;
+  int32_t merge_begin;
+  int32_t num_merges;
+  int32_t num_qo_heads;
+  int32_t group;
+};
+
+// Standalone merge over [rows, splits, heads, D] partials with natural-log lse.
+struct MergeDenseArgs {
+  const float* o_part;
+  const float* lse_part;
+  void* o;
+  float* lse;
+  int64_t num_rows;
+  int32_t num_splits;
+  int32_t num_heads;
+  int32_t head_dim;
+};
+
+}  // namespace dpp

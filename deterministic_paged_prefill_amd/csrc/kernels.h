@@ -1,0 +1,20 @@
+// Host-side launchers of the device kernels (defined in prefill.hip and merge.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "dpp_internal.h"
+
+namespace dpp {
+
+// One prefill pass: grid (num_items, num_kv_heads), kThreads threads, dynamic LDS for the
+// tile buffers and the item's page-id table.
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
+
+// Merge of the split partials of one pass: grid (num_merges, num_kv_heads).
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream);
+
+// Standalone merge over dense [rows, splits, heads, D] partials.
+hipError_t launch_merge_dense(const MergeDenseArgs& a, hipStream_t stream);
+
+}  // namespace dpp

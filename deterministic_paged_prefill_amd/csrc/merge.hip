@@ -1,0 +1,144 @@
+// Deterministic merge of split partial states, gfx950.
+//
+// A row whose keys reach past one 4096-token split leaves one partial (o_s, lse2_s) per split
+// (o_s normalised by its own sum, lse2_s the split's base-2 log-sum-exp). The combined row is
+//   M   = max_s lse2_s
+//   w_s = 1 if lse2_s == M else exp2(lse2_s - M)
+//   o   = (sum_s w_s o_s) / (sum_s w_s),  sums taken in ascending s (fma chain / plain adds)
+//   lse = (M + log2(sum_s w_s)) * ln 2
+// -- the softmax over the union of the splits' keys. Rows are independent and each is
+// combined by one thread group in a fixed order: no atomics, no dependence on how many rows
+// or tiles share the launch. Sources: fixed KV splits with partial-result buffers
+// (model-serving-minefield issue #73, correction comment, "What the flag actually does",
+// item 2, and "The failure"); the benchmark spec's fixed-order merge-states kernel.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "dpp_internal.h"
+#include "kernels.h"
+
+namespace dpp {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLn2 = 0.693147180559945309417f;
+constexpr float kLog2e = 1.44269504088896340736f;
+
+__device__ inline uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 a = (__bf16)lo;
+  const __bf16 b = (__bf16)hi;
+  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// Combine S partials of one row for 4 consecutive columns. lse2_at(s) gives the split's
+// base-2 lse (-inf = empty partial, skipped), o_at(s) its 4 columns. Returns the combined
+// columns and writes the combined base-2 lse (or -inf) to *lse2_out.
+template <class LseAt, class OAt>
+__device__ inline f32x4 merge4(int S, LseAt lse2_at, OAt o_at, float* lse2_out) {
+  float M = -INFINITY;
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lse2_at(s));
+  if (M == -INFINITY) {
+    *lse2_out = -INFINITY;
+    return f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+  for (int s = 0; s < S; ++s) {
+    const float l2 = lse2_at(s);
+    if (l2 == -INFINITY) continue;
+    const float w = (l2 == M) ? 1.f : __builtin_amdgcn_exp2f(l2 - M);
+    const f32x4 os = o_at(s);
+    num[0] = __builtin_fmaf(w, os[0], num[0]);
+    num[1] = __builtin_fmaf(w, os[1], num[1]);
+    num[2] = __builtin_fmaf(w, os[2], num[2]);
+    num[3] = __builtin_fmaf(w, os[3], num[3]);
+    den = den + w;
+  }
+  const float inv = 1.f / den;
+  *lse2_out = M + __builtin_amdgcn_logf(den);
+  return f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+}
+
+// Planned merge: grid (merges in pass, kv heads); each block merges one q tile's rows.
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+  constexpr int kTpr = D / 4;              // threads per row (4 columns each)
+  constexpr int kRowsPerPass = kThreads / kTpr;
+  const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
+  const MergeItem mi = reinterpret_cast<const MergeItem*>(a.header + pre->merge_offset)[a.merge_begin + blockIdx.x];
+  const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[mi.request];
+  const int kvh = blockIdx.y;
+  const int g = a.group;
+  const int tile_rows = min(kBlockM, rq.qo_len * g - mi.row_start);
+  const int ctx = rq.kv_len - rq.qo_len;
+  const int col = (threadIdx.x % kTpr) * 4;
+  for (int lr = threadIdx.x / kTpr; lr < tile_rows; lr += kRowsPerPass) {
+    const int R = mi.row_start + lr;
+    const int token = R / g;
+    const int p = ctx + token;
+    const int S = p / kSplitTokens + 1;
+    if (S < 2) continue;  // finished by the prefill kernel
+    auto lse_at = [&](int s) {
+      return a.part_lse2[partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr)];
+    };
+    auto o_at = [&](int s) {
+      return *reinterpret_cast<const f32x4*>(a.part_o + partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr) * D + col);
+    };
+    float lse2;
+    const f32x4 o = merge4(S, lse_at, o_at, &lse2);
+    const int64_t orow = (int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + orow * D + col) =
+        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    if (col == 0) a.lse[orow] = lse2 * kLn2;
+  }
+}
+
+// Standalone merge: one wave per (row, head); natural-log lse converted to base 2 on load.
+__global__ __launch_bounds__(kThreads) void merge_dense_kernel(MergeDenseArgs a) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int64_t rh = (int64_t)blockIdx.x * kWaves + wave;
+  if (rh >= a.num_rows * a.num_heads) return;
+  const int64_t r = rh / a.num_heads;
+  const int h = (int)(rh - r * a.num_heads);
+  const int S = a.num_splits;
+  const int H = a.num_heads;
+  const int D = a.head_dim;
+  for (int col = lane * 4; col < D; col += 256) {
+    auto lse_at = [&](int s) { return a.lse_part[(r * S + s) * H + h] * kLog2e; };
+    auto o_at = [&](int s) {
+      return *reinterpret_cast<const f32x4*>(a.o_part + ((r * S + s) * H + h) * (int64_t)D + col);
+    };
+    float lse2;
+    const f32x4 o = merge4(S, lse_at, o_at, &lse2);
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(a.o) + rh * D + col) =
+        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+    if (col == 0) a.lse[rh] = lse2 * kLn2;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream) {
+  dim3 grid((unsigned)a.num_merges, (unsigned)num_kv_heads);
+  if (head_dim == 128)
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+  else if (head_dim == 256)
+    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, a);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_dense(const MergeDenseArgs& a, hipStream_t stream) {
+  const int64_t waves = a.num_rows * a.num_heads;
+  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(merge_dense_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace dpp

@@ -1,0 +1,289 @@
+// Host planner: batch shape -> work list. Pure integer host code; no HIP calls.
+//
+// What it decides, and what it never decides:
+//  * tile geometry (kBlockM packed rows x kBlockN keys) and the 4096-token split length are
+//    constants; nothing here reads the batch's average or maximum query length (the sglang
+//    PR #46351 page, "Root cause", is the failure this avoids);
+//  * a request's query block is right-aligned to its KV: row i sits at position
+//    kv_len - qo_len + i (same page, "Fix" section);
+//  * a q tile visits KV tiles 0 .. floor(p_max / 64) of every split its last row reaches;
+//    rows needing one split finish in the prefill kernel, longer rows leave one partial per
+//    split in the workspace and are combined by the merge kernel;
+//  * passes: partials are bounded by the caller's cap by running tiles in several launches
+//    (the model-serving-minefield issue #73 correction, "The failure", shows an unbounded
+//    split buffer crashing a server);
+//  * order: items of a pass are sorted longest first for load balance. Order, passes and cap
+//    change when and where a row is computed, never its arithmetic.
+#include "plan.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <limits>
+#include <memory>
+#include <new>
+
+namespace dpp {
+
+static thread_local std::string g_last_error;
+
+void set_error(const std::string& msg) { g_last_error = msg; }
+
+dpp_status fail(dpp_status st, const std::string& msg) {
+  g_last_error = msg;
+  return st;
+}
+
+namespace {
+
+struct TileInfo {
+  int32_t request;
+  int32_t row_start;
+  int32_t rows;
+  int64_t p_max;
+  int32_t splits;
+  int32_t pass = 0;
+  int64_t slot_base = -1;
+};
+
+// Largest slot count n with align(n*D*4) + align(n*4) <= avail.
+int64_t max_slots_for(size_t avail, int head_dim) {
+  const size_t per_slot = (size_t)(head_dim + 1) * 4;
+  int64_t n = (int64_t)(avail / per_slot);
+  while (n > 0 && align_up((size_t)n * head_dim * 4, 256) + align_up((size_t)n * 4, 256) > avail) --n;
+  return n;
+}
+
+}  // namespace
+}  // namespace dpp
+
+using namespace dpp;
+
+extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
+                                      const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                      const int32_t* last_page_len, size_t workspace_cap,
+                                      dpp_plan** out_plan) {
+  if (out_plan) *out_plan = nullptr;
+  if (!cfg || !out_plan) return fail(DPP_ERR_INVALID, "dpp_plan_create: null cfg or out_plan");
+  if (batch_size < 0) return fail(DPP_ERR_INVALID, "dpp_plan_create: negative batch_size");
+  if (!qo_indptr || !kv_indptr || (batch_size > 0 && !last_page_len))
+    return fail(DPP_ERR_INVALID, "dpp_plan_create: null index array");
+
+  const dpp_config c = *cfg;
+  if (c.num_qo_heads <= 0 || c.num_kv_heads <= 0 || c.num_qo_heads % c.num_kv_heads != 0)
+    return fail(DPP_ERR_UNSUPPORTED,
+                "num_qo_heads must be a positive multiple of num_kv_heads (got " +
+                    std::to_string(c.num_qo_heads) + "/" + std::to_string(c.num_kv_heads) + ")");
+  if (c.head_dim != 128 && c.head_dim != 256)
+    return fail(DPP_ERR_UNSUPPORTED, "head_dim " + std::to_string(c.head_dim) +
+                                         " not built (128 and 256 are)");
+  if (c.page_size < 1 || c.page_size > 1024)
+    return fail(DPP_ERR_UNSUPPORTED, "page_size must be in [1, 1024]");
+  if (c.kv_dtype != DPP_KV_BF16 && c.kv_dtype != DPP_KV_FP8_E4M3)
+    return fail(DPP_ERR_UNSUPPORTED, "kv_dtype must be DPP_KV_BF16 or DPP_KV_FP8_E4M3");
+  if (!(c.sm_scale >= 0.f) || !std::isfinite(c.sm_scale))
+    return fail(DPP_ERR_INVALID, "sm_scale must be finite and >= 0");
+  if (c.kv_dtype == DPP_KV_FP8_E4M3 &&
+      (!std::isfinite(c.k_scale) || !std::isfinite(c.v_scale) || c.k_scale <= 0.f || c.v_scale <= 0.f))
+    return fail(DPP_ERR_INVALID, "fp8 k_scale / v_scale must be finite and > 0");
+
+  if (qo_indptr[0] != 0 || kv_indptr[0] != 0)
+    return fail(DPP_ERR_INVALID, "qo_indptr[0] and kv_indptr[0] must be 0");
+  const int32_t group = c.num_qo_heads / c.num_kv_heads;
+  const int64_t P = c.page_size;
+
+  std::vector<RequestDesc> reqs((size_t)batch_size);
+  std::vector<TileInfo> tiles;
+  for (int32_t r = 0; r < batch_size; ++r) {
+    const int64_t qo_len = (int64_t)qo_indptr[r + 1] - qo_indptr[r];
+    const int64_t np = (int64_t)kv_indptr[r + 1] - kv_indptr[r];
+    if (qo_len < 0 || np < 0)
+      return fail(DPP_ERR_INVALID, "indptr not non-decreasing at request " + std::to_string(r));
+    int64_t kv_len = 0;
+    if (np > 0) {
+      if (last_page_len[r] < 1 || last_page_len[r] > c.page_size)
+        return fail(DPP_ERR_SHAPE, "kv_last_page_len[" + std::to_string(r) + "] = " +
+                                       std::to_string(last_page_len[r]) + " outside [1, page_size]");
+      kv_len = (np - 1) * P + last_page_len[r];
+    }
+    if (kv_len > std::numeric_limits<int32_t>::max() / 2)
+      return fail(DPP_ERR_UNSUPPORTED, "kv_len too large at request " + std::to_string(r));
+    if (qo_len > kv_len)
+      return fail(DPP_ERR_SHAPE, "request " + std::to_string(r) + ": qo_len " +
+                                     std::to_string(qo_len) + " > kv_len " + std::to_string(kv_len));
+    reqs[(size_t)r] = RequestDesc{qo_indptr[r], (int32_t)qo_len, kv_indptr[r], (int32_t)kv_len};
+    const int64_t packed = qo_len * group;
+    if (packed > std::numeric_limits<int32_t>::max() - kBlockM)
+      return fail(DPP_ERR_UNSUPPORTED, "too many query rows in request " + std::to_string(r));
+    for (int64_t rs = 0; rs < packed; rs += kBlockM) {
+      TileInfo t{};
+      t.request = r;
+      t.row_start = (int32_t)rs;
+      t.rows = (int32_t)std::min<int64_t>(kBlockM, packed - rs);
+      t.p_max = kv_len - qo_len + (rs + t.rows - 1) / group;
+      t.splits = (int32_t)(t.p_max / kSplitTokens + 1);
+      tiles.push_back(t);
+    }
+  }
+
+  int64_t n_items = 0, n_merges = 0;
+  for (const auto& t : tiles) {
+    n_items += t.splits;
+    n_merges += t.splits > 1 ? 1 : 0;
+  }
+  const int64_t words = kHeaderWords + 4 * (int64_t)batch_size + 8 * n_items + 4 * n_merges;
+  if (n_items > std::numeric_limits<int32_t>::max() / 2 || words > std::numeric_limits<int32_t>::max() / 2)
+    return fail(DPP_ERR_UNSUPPORTED, "batch too large for one plan");
+  const size_t header_bytes = align_up((size_t)words * 4, 256);
+
+  int64_t slot_limit = std::numeric_limits<int32_t>::max() / 2;
+  if (workspace_cap > 0) {
+    if (workspace_cap < header_bytes)
+      return fail(DPP_ERR_WORKSPACE, "workspace cap " + std::to_string(workspace_cap) +
+                                         " B is below the work list's " +
+                                         std::to_string(header_bytes) + " B");
+    slot_limit = std::min<int64_t>(slot_limit, max_slots_for(workspace_cap - header_bytes, c.head_dim));
+  }
+
+  // Passes: tiles in request order; a tile needing partials takes S_t * Hkv * kBlockM slots.
+  int32_t pass = 0;
+  int64_t used = 0, max_used = 0;
+  for (auto& t : tiles) {
+    const int64_t need = t.splits > 1 ? (int64_t)t.splits * c.num_kv_heads * kBlockM : 0;
+    if (need > slot_limit)
+      return fail(DPP_ERR_WORKSPACE,
+                  "workspace cap too small: one q tile needs " +
+                      std::to_string(need * (c.head_dim + 1) * 4 + header_bytes) + " B");
+    if (used + need > slot_limit) {
+      ++pass;
+      used = 0;
+    }
+    t.pass = pass;
+    if (need > 0) {
+      t.slot_base = used;
+      used += need;
+      max_used = std::max(max_used, used);
+    }
+  }
+  const int32_t num_passes = tiles.empty() ? 0 : pass + 1;
+
+  std::unique_ptr<dpp_plan> plan(new (std::nothrow) dpp_plan());
+  if (!plan) return fail(DPP_ERR_INVALID, "out of host memory");
+  plan->cfg = c;
+  if (plan->cfg.sm_scale == 0.f) plan->cfg.sm_scale = (float)(1.0 / std::sqrt((double)c.head_dim));
+  if (c.kv_dtype == DPP_KV_BF16) plan->cfg.k_scale = plan->cfg.v_scale = 1.f;
+  plan->group = group;
+  plan->scale_log2 = (float)((double)plan->cfg.sm_scale * 1.4426950408889634);
+  plan->batch_size = batch_size;
+  plan->total_q_rows = batch_size > 0 ? qo_indptr[batch_size] : 0;
+  plan->num_items = (int32_t)n_items;
+  plan->num_merges = (int32_t)n_merges;
+
+  // Emit items pass by pass, longest first inside a pass (stable, so ties keep tile order).
+  std::vector<PrefillItem> items;
+  std::vector<MergeItem> merges;
+  items.reserve((size_t)n_items);
+  merges.reserve((size_t)n_merges);
+  plan->item_pass.assign(1, 0);
+  plan->merge_pass.assign(1, 0);
+  int64_t max_page_span = 1;
+  size_t tile_cursor = 0;
+  for (int32_t p = 0; p < num_passes; ++p) {
+    const size_t first = items.size();
+    while (tile_cursor < tiles.size() && tiles[tile_cursor].pass == p) {
+      const TileInfo& t = tiles[tile_cursor++];
+      const RequestDesc& rq = reqs[(size_t)t.request];
+      const int64_t last_tile = t.p_max / kBlockN;
+      for (int32_t s = 0; s < t.splits; ++s) {
+        PrefillItem it{};
+        it.request = t.request;
+        it.row_start = t.row_start;
+        it.split = s;
+        it.tile_splits = t.splits;
+        it.kv_tile_begin = s * kTilesPerSplit;
+        it.kv_tile_end = (int32_t)std::min<int64_t>((int64_t)(s + 1) * kTilesPerSplit, last_tile + 1);
+        it.slot_base = (int32_t)t.slot_base;
+        const int64_t key_lo = (int64_t)it.kv_tile_begin * kBlockN;
+        const int64_t key_hi = std::min<int64_t>((int64_t)it.kv_tile_end * kBlockN, rq.kv_len);
+        if (key_hi > key_lo) max_page_span = std::max(max_page_span, (key_hi - 1) / P - key_lo / P + 1);
+        items.push_back(it);
+      }
+      if (t.splits > 1) merges.push_back(MergeItem{t.request, t.row_start, t.splits, (int32_t)t.slot_base});
+    }
+    std::stable_sort(items.begin() + (std::ptrdiff_t)first, items.end(),
+                     [](const PrefillItem& a, const PrefillItem& b) {
+                       return (a.kv_tile_end - a.kv_tile_begin) > (b.kv_tile_end - b.kv_tile_begin);
+                     });
+    plan->item_pass.push_back((int32_t)items.size());
+    plan->merge_pass.push_back((int32_t)merges.size());
+  }
+
+  // Serialise: preamble | requests | items | merges.
+  plan->header.assign((size_t)words, 0);
+  HeaderPreamble pre{};
+  pre.magic = kHeaderMagic;
+  pre.num_requests = batch_size;
+  pre.num_items = (int32_t)n_items;
+  pre.num_merges = (int32_t)n_merges;
+  pre.request_offset = kHeaderWords;
+  pre.item_offset = kHeaderWords + 4 * batch_size;
+  pre.merge_offset = pre.item_offset + 8 * (int32_t)n_items;
+  std::memcpy(plan->header.data(), &pre, sizeof pre);
+  if (batch_size > 0)
+    std::memcpy(plan->header.data() + pre.request_offset, reqs.data(), reqs.size() * sizeof(RequestDesc));
+  if (!items.empty())
+    std::memcpy(plan->header.data() + pre.item_offset, items.data(), items.size() * sizeof(PrefillItem));
+  if (!merges.empty())
+    std::memcpy(plan->header.data() + pre.merge_offset, merges.data(), merges.size() * sizeof(MergeItem));
+
+  plan->max_partial_slots = max_used;
+  plan->header_bytes = header_bytes;
+  plan->partial_o_offset = header_bytes;
+  plan->partial_lse_offset = header_bytes + align_up((size_t)max_used * c.head_dim * 4, 256);
+  plan->workspace_bytes = plan->partial_lse_offset + align_up((size_t)max_used * 4, 256);
+  plan->page_slots = (int32_t)max_page_span;
+  *out_plan = plan.release();
+  return DPP_OK;
+}
+
+extern "C" size_t dpp_plan_workspace_bytes(const dpp_plan* plan) {
+  return plan ? plan->workspace_bytes : 0;
+}
+
+extern "C" dpp_status dpp_plan_get_info(const dpp_plan* plan, dpp_plan_info* info) {
+  if (!plan || !info) return fail(DPP_ERR_INVALID, "dpp_plan_get_info: null argument");
+  info->block_m = kBlockM;
+  info->block_n = kBlockN;
+  info->split_tokens = kSplitTokens;
+  info->num_passes = (int32_t)plan->item_pass.size() - 1;
+  info->num_prefill_items = plan->num_items;
+  info->num_merge_items = plan->num_merges;
+  info->max_partial_slots = plan->max_partial_slots;
+  info->header_bytes = plan->header_bytes;
+  info->workspace_bytes = plan->workspace_bytes;
+  info->total_q_rows = plan->total_q_rows;
+  return DPP_OK;
+}
+
+extern "C" dpp_status dpp_plan_header(const dpp_plan* plan, const void** data, size_t* bytes) {
+  if (!plan || !data || !bytes) return fail(DPP_ERR_INVALID, "dpp_plan_header: null argument");
+  *data = plan->header.data();
+  *bytes = plan->header.size() * sizeof(int32_t);
+  return DPP_OK;
+}
+
+extern "C" const char* dpp_last_error(void) { return g_last_error.c_str(); }
+
+extern "C" const char* dpp_status_string(dpp_status st) {
+  switch (st) {
+    case DPP_OK: return "DPP_OK";
+    case DPP_ERR_INVALID: return "DPP_ERR_INVALID";
+    case DPP_ERR_SHAPE: return "DPP_ERR_SHAPE";
+    case DPP_ERR_UNSUPPORTED: return "DPP_ERR_UNSUPPORTED";
+    case DPP_ERR_WORKSPACE: return "DPP_ERR_WORKSPACE";
+    case DPP_ERR_HIP: return "DPP_ERR_HIP";
+  }
+  return "DPP_ERR_UNKNOWN";
+}
+
+extern "C" int32_t dpp_abi_version(void) { return 1; }

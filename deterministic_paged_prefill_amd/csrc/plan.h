@@ -1,0 +1,50 @@
+// Host planner of libdpp: turns one batch shape into the work list the kernels run.
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/dpp.h"
+#include "dpp_internal.h"
+
+struct dpp_plan {
+  dpp_config cfg{};
+  int32_t group = 1;
+  float scale_log2 = 0.f;  // sm_scale * log2(e), rounded once to fp32
+  int32_t batch_size = 0;
+  int64_t total_q_rows = 0;
+
+  // Work list (int32 words): preamble, requests, prefill items, merge items.
+  std::vector<int32_t> header;
+  int32_t num_items = 0;
+  int32_t num_merges = 0;
+
+  // Pass p runs prefill items [item_pass[p], item_pass[p+1]) and merge items
+  // [merge_pass[p], merge_pass[p+1]).
+  std::vector<int32_t> item_pass;
+  std::vector<int32_t> merge_pass;
+
+  int64_t max_partial_slots = 0;
+  size_t header_bytes = 0;
+  size_t partial_o_offset = 0;    // byte offsets inside the workspace
+  size_t partial_lse_offset = 0;
+  size_t workspace_bytes = 0;
+  int32_t page_slots = 0;         // LDS page-id entries one item may need
+
+  // Pinned host copy of `header`, created on first dpp_run (plan creation stays HIP-free).
+  mutable std::mutex pinned_mu;
+  mutable void* pinned = nullptr;
+};
+
+namespace dpp {
+
+// Thread-local error text behind dpp_last_error().
+void set_error(const std::string& msg);
+dpp_status fail(dpp_status st, const std::string& msg);
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace dpp

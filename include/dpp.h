@@ -1,0 +1,179 @@
+/*
+ * dpp.h -- C ABI of libdpp: batch-invariant causal GQA prefill attention over a paged KV
+ * cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (north_star definition; causal placement from sglang PR #46351, "Fix"
+ * section and the author's reply on tail alignment): for request r with qo_len query tokens
+ * and kv_len cached-plus-new tokens, query row i of q head h attends to keys 0..p of kv head
+ * h / (num_qo_heads / num_kv_heads), where p = kv_len - qo_len + i, and returns
+ *
+ *     o[i, h, :]  = softmax_j( sm_scale * <q[i, h, :], k[j, :]> ) @ v[j, :]      (bf16)
+ *     lse[i, h]   = log sum_j exp( sm_scale * <q[i, h, :], k[j, :]> )            (fp32, natural log)
+ *
+ * Batch invariance is the contract: the bits of a row depend only on its own query, keys
+ * 0..p and the configuration below -- never on the other requests in the batch, on qo_len
+ * (a prefix-cache hit that sends only the uncached tail returns exactly the rows of the full
+ * prefill), on page placement, or on the workspace cap. The sglang PR #46351 page ("Root
+ * cause") traces the failure of this contract in FlashInfer to a q-tile size chosen from the
+ * batch's average query length; here every tile size, KV chunk and reduction order is a
+ * constant of (num_qo_heads, num_kv_heads, head_dim).
+ *
+ * Long rows are cut into fixed KV splits of 4096 tokens at absolute positions 0, 4096, ...
+ * (model-serving-minefield issue #73, correction comment, "What the flag actually does",
+ * item 2). Each split's partial state goes to a caller-owned workspace whose size the plan
+ * bounds (that page's "The failure" section describes the unbounded version killing a
+ * server); a merge kernel then combines a row's partials in ascending split order.
+ *
+ * Memory layout (all device buffers are caller-owned; the library never allocates or frees
+ * device memory and never synchronises a stream):
+ *   q          [qo_indptr[B], num_qo_heads, head_dim]            bf16, contiguous
+ *   k_pool     [num_pages, page_size, num_kv_heads, head_dim]     bf16 or fp8 E4M3 (OCP), contiguous
+ *   v_pool     same as k_pool
+ *   kv_indices [kv_indptr[B]] int32 page ids; request r owns kv_indices[kv_indptr[r] .. kv_indptr[r+1])
+ *   o          [qo_indptr[B], num_qo_heads, head_dim]             bf16
+ *   lse        [qo_indptr[B], num_qo_heads]                       fp32 (natural log)
+ * Request r's KV is kv_len = (pages - 1) * page_size + kv_last_page_len[r] tokens (0 if it
+ * owns no pages); token j lives in page kv_indices[kv_indptr[r] + j / page_size], slot
+ * j % page_size. Slots past a request's kv_len are never read.
+ *
+ * Errors: every entry point returns a dpp_status and, on failure, records a message that
+ * dpp_last_error() returns (thread-local). Nothing aborts, exits or throws across the ABI.
+ */
+#ifndef DPP_H
+#define DPP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DPP_OK = 0,
+  DPP_ERR_INVALID = 1,     /* null pointer, negative count, non-monotone or non-zero-based indptr */
+  DPP_ERR_SHAPE = 2,       /* qo_len > kv_len, last-page length outside [1, page_size], q row
+                              count != qo_indptr[B] (the check sglang PR #46351 reports as a
+                              ValueError from FlashInfer's paged prefill) */
+  DPP_ERR_UNSUPPORTED = 3, /* head_dim, page_size, head counts or kv dtype not built */
+  DPP_ERR_WORKSPACE = 4,   /* workspace smaller than the plan needs, misaligned, or a cap too
+                              small for one q tile's partials; reported before any launch */
+  DPP_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed */
+} dpp_status;
+
+typedef enum { DPP_KV_BF16 = 0, DPP_KV_FP8_E4M3 = 1 } dpp_kv_dtype;
+
+/* Model-level constants. These, and only these, fix the arithmetic of every row. */
+typedef struct {
+  int32_t num_qo_heads;  /* Hq, a multiple of num_kv_heads */
+  int32_t num_kv_heads;  /* Hkv */
+  int32_t head_dim;      /* 128 or 256 */
+  int32_t page_size;     /* tokens per page, 1..1024 */
+  int32_t kv_dtype;      /* dpp_kv_dtype */
+  float sm_scale;        /* softmax scale; 0 selects 1/sqrt(head_dim) */
+  float k_scale;         /* fp8 dequantisation multipliers (value = decode(code) * scale);
+                            ignored for bf16. Powers of two make the bf16 staging exact. */
+  float v_scale;
+} dpp_config;
+
+/* Opaque host-side plan: the work list of one batch shape. Created from host copies of the
+ * index arrays, reusable for every layer that runs on that batch. */
+typedef struct dpp_plan dpp_plan;
+
+/* Read-only facts about a plan (for tests and reporting). */
+typedef struct {
+  int32_t block_m;            /* packed query rows (token x q head of a group) per tile */
+  int32_t block_n;            /* keys per KV tile, tiles start at multiples of block_n */
+  int32_t split_tokens;       /* fixed KV split length (4096) */
+  int32_t num_passes;         /* launches of (prefill, merge) needed under the cap */
+  int64_t num_prefill_items;  /* (q tile, split) work items, all passes, per kv head */
+  int64_t num_merge_items;    /* q tiles needing a merge, all passes, per kv head */
+  int64_t max_partial_slots;  /* partial rows of the largest pass (each (head_dim+1)*4 bytes) */
+  size_t header_bytes;        /* work list uploaded at the head of the workspace */
+  size_t workspace_bytes;     /* what dpp_run needs */
+  int64_t total_q_rows;       /* qo_indptr[B] */
+} dpp_plan_info;
+
+/*
+ * Build the plan of one batch. Host only: no HIP call, no device memory.
+ *
+ *   cfg                  model constants (copied)
+ *   batch_size           B >= 0
+ *   qo_indptr_host       [B+1] int32, qo_indptr[0] == 0, non-decreasing
+ *   kv_indptr_host       [B+1] int32, kv_indptr[0] == 0, non-decreasing (page counts)
+ *   kv_last_page_len_host[B]  int32, in [1, page_size] for every request with pages
+ *   workspace_cap_bytes  upper bound on dpp_plan_workspace_bytes(); 0 = no bound. Rows whose
+ *                        partials do not fit are run in further passes; the cap changes the
+ *                        number of launches, never a bit of the result.
+ *   out_plan             receives the plan (NULL on failure); free with dpp_plan_destroy
+ *
+ * Errors: DPP_ERR_INVALID (null pointers, bad indptr), DPP_ERR_SHAPE (qo_len > kv_len, last
+ * page length out of range), DPP_ERR_UNSUPPORTED (config), DPP_ERR_WORKSPACE (cap below the
+ * smallest pass).
+ */
+dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
+                           const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                           const int32_t* kv_last_page_len_host, size_t workspace_cap_bytes,
+                           dpp_plan** out_plan);
+
+/* Bytes of device workspace dpp_run needs for this plan (256-byte aligned buffer). */
+size_t dpp_plan_workspace_bytes(const dpp_plan* plan);
+
+/* Fill *info. DPP_ERR_INVALID on null arguments. */
+dpp_status dpp_plan_get_info(const dpp_plan* plan, dpp_plan_info* info);
+
+/* The work list exactly as dpp_run uploads it (host memory owned by the plan, valid until
+ * dpp_plan_destroy). Layout: int32 words; see the planner source for the record format. */
+dpp_status dpp_plan_header(const dpp_plan* plan, const void** data, size_t* bytes);
+
+/* Free a plan. The plan must outlive the stream work of every dpp_run that used it (the
+ * upload of its work list reads the plan's pinned host buffer asynchronously). NULL is a no-op. */
+void dpp_plan_destroy(dpp_plan* plan);
+
+/*
+ * Run the planned attention on `stream` (a hipStream_t; NULL = the null stream).
+ *
+ *   q, k_pool, v_pool, kv_indices, o, lse   device pointers, layouts above
+ *   q_rows        rows of q and o; must equal qo_indptr[B] of the plan (DPP_ERR_SHAPE)
+ *   num_pages     pages in each pool; a page id outside [0, num_pages) reads as zeros
+ *   workspace     device buffer of at least dpp_plan_workspace_bytes(plan) bytes, 256-byte
+ *                 aligned; its contents are scratch (work list + split partials)
+ *
+ * Enqueues: one async copy of the work list into the workspace, then per pass one prefill
+ * launch and (if some row spans several splits) one merge launch. Returns without waiting.
+ * On DPP_ERR_SHAPE / DPP_ERR_WORKSPACE / DPP_ERR_UNSUPPORTED nothing is enqueued.
+ */
+dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows, const void* k_pool,
+                   const void* v_pool, int64_t num_pages, const int32_t* kv_indices, void* o,
+                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Combine softmax partial states, the same device merge dpp_run uses for split rows.
+ *
+ *   o_partial   [num_rows, num_splits, num_heads, head_dim] fp32 device
+ *   lse_partial [num_rows, num_splits, num_heads] fp32 device, natural log; -inf marks an
+ *               empty partial (weight 0)
+ *   o           [num_rows, num_heads, head_dim] bf16 device out
+ *   lse         [num_rows, num_heads] fp32 device out (natural log)
+ * Partials are combined in ascending split order with weights exp(lse_s - max_s lse_s).
+ * A row whose partials are all empty gets o = 0, lse = -inf.
+ * head_dim must be a multiple of 4 and at most 1024; num_splits in [1, 1024].
+ */
+dpp_status dpp_merge_states(const float* o_partial, const float* lse_partial, int64_t num_rows,
+                            int32_t num_splits, int32_t num_heads, int32_t head_dim, void* o,
+                            float* lse, void* stream);
+
+/* Message of the last failing call on this thread ("" if none). */
+const char* dpp_last_error(void);
+
+/* Name of a status code. */
+const char* dpp_status_string(dpp_status status);
+
+/* ABI version of the library (bumped when a signature or record format changes). */
+int32_t dpp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DPP_H */

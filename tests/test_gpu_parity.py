@@ -1,0 +1,168 @@
+"""GPU parity: libdpp against the fp64 oracle on every configuration, plus cached-vs-full
+bit-exactness on the configurations that define it.
+
+Tolerances: max |o - oracle| <= 1e-2 on bf16 outputs, max |lse - oracle| <= 2e-3 on fp32 lse.
+Bit-exactness: the cached tail's rows equal the full prefill's rows bit for bit (o and lse).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads as wl
+from gpu_helpers import (Device, assert_bits_equal, assert_close_to_oracle, oracle_rows,
+                         sample_rows, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def oracle():
+    import oracle as o
+    o.build(force=False)
+    return o
+
+
+def _check_pairs(cached_batch, o_c, l_c, full_batch, o_f, l_f, pairs, what):
+    for rc, rf in pairs:
+        assert cached_batch.requests[rc].qo_len < cached_batch.requests[rc].kv_len, "the hit is real"
+        ia, ib = wl.matching_rows(cached_batch, rc, full_batch, rf)
+        assert len(ia) == cached_batch.requests[rc].qo_len
+        assert_bits_equal(o_c[ia], o_f[ib], f"{what} o req {rc}")
+        assert_bits_equal(l_c[ia], l_f[ib], f"{what} lse req {rc}")
+
+
+def test_config1_single_extend(oracle):
+    work = wl.config1_single_extend()
+    dev = Device(work)
+    full, cached = work.batches["full"], work.batches["cached"]
+    o_f, l_f = dev.run(full)
+    o_c, l_c = dev.run(cached)
+    for b, o, l, name in ((full, o_f, l_f, "full"), (cached, o_c, l_c, "cached")):
+        ro, rl = oracle_rows(oracle, work, b)
+        assert_close_to_oracle(o, l, ro, rl, what=f"config1 {name}")
+    _check_pairs(cached, o_c, l_c, full, o_f, l_f, [(0, 0)], "config1")
+
+
+RANDOM_CASES = [
+    # (seed, hq, hkv, d, page, kv_dtype, specs [(prompt_len, qo_len)])
+    (1, 32, 8, 128, 16, "bf16", [(1, 1), (2, 2), (63, 63), (64, 64), (65, 65), (67, 3), (300, 0), (129, 1)]),
+    (2, 32, 8, 128, 1, "bf16", [(200, 17), (97, 97), (33, 32)]),
+    (3, 32, 8, 128, 5, "bf16", [(150, 150), (151, 2), (40, 39)]),
+    (4, 8, 8, 128, 64, "bf16", [(180, 180), (181, 35), (7, 7)]),
+    (5, 16, 2, 128, 16, "bf16", [(130, 130), (257, 16)]),
+    (6, 24, 4, 256, 16, "bf16", [(160, 160), (161, 5), (70, 1)]),
+    (7, 24, 4, 256, 16, "fp8_e4m3", [(160, 160), (161, 5), (70, 1)]),
+    (8, 32, 8, 128, 16, "fp8_e4m3", [(140, 140), (141, 9)]),
+    (9, 32, 8, 128, 16, "bf16", [(4100, 12), (4096, 3), (4097, 1), (8200, 2)]),
+    (10, 24, 4, 256, 16, "fp8_e4m3", [(4100, 30), (8193, 1)]),
+]
+
+
+@pytest.mark.parametrize("case", RANDOM_CASES, ids=[f"seed{c[0]}" for c in RANDOM_CASES])
+def test_random_against_oracle(oracle, case):
+    seed, hq, hkv, d, page, kv_dtype, specs = case
+    work = wl.random_workload(seed, hq=hq, hkv=hkv, d=d, page_size=page, kv_dtype=kv_dtype,
+                              specs=specs)
+    dev = Device(work)
+    batch = work.batches["batch"]
+    o, l = dev.run(batch)
+    ro, rl = oracle_rows(oracle, work, batch)
+    assert_close_to_oracle(o, l, ro, rl, what=f"random seed {seed}")
+    # the same rows inside full prefills, placed in other pages, are bit-identical
+    full = work.batches["full"]
+    o_f, l_f = dev.run(full)
+    pairs = [(i, i) for i in range(len(specs)) if 0 < batch.requests[i].qo_len < batch.requests[i].kv_len]
+    _check_pairs(batch, o, l, full, o_f, l_f, pairs, f"random seed {seed}")
+
+
+@pytest.mark.parametrize("layout", ["radix", "distinct"])
+def test_config2_extend_batch(oracle, layout):
+    work = wl.config2_extend_batch(layout=layout)
+    dev = Device(work)
+    cached, full = work.batches["cached"], work.batches["full"]
+    o_c, l_c = dev.run(cached)
+    ro, rl = oracle_rows(oracle, work, cached)
+    assert_close_to_oracle(o_c, l_c, ro, rl, what=f"config2 {layout}")
+    o_f, l_f = dev.run(full)
+    _check_pairs(cached, o_c, l_c, full, o_f, l_f, [(i, i) for i in range(16)], f"config2 {layout}")
+    # each extend alone gives the same bits as inside the batch
+    for i in (0, 7, 15):
+        one = wl.sub_batch(cached, work.prompts, work.page_size, [i])
+        o1, l1 = dev.run(one)
+        a, b = int(cached.qo_indptr[i]), int(cached.qo_indptr[i + 1])
+        assert_bits_equal(o1, o_c[a:b], f"config2 request {i} alone vs batched")
+        assert_bits_equal(l1, l_c[a:b], f"config2 request {i} alone vs batched (lse)")
+
+
+def test_config3_cold_prefill(oracle):
+    work = wl.config3_cold_prefill()
+    dev = Device(work)
+    full = work.batches["full"]
+    o, l = dev.run(full)
+    rows = sample_rows(full, 24, seed=3)
+    ro, rl = oracle_rows(oracle, work, full, rows)
+    assert_close_to_oracle(o, l, ro, rl, rows=rows, what="config3 sampled rows")
+    for i in (0, 9):
+        one = wl.sub_batch(full, work.prompts, work.page_size, [i])
+        o1, l1 = dev.run(one)
+        a, b = int(full.qo_indptr[i]), int(full.qo_indptr[i + 1])
+        assert_bits_equal(o1, o[a:b], f"config3 request {i} alone vs batch of 16")
+        assert_bits_equal(l1, l[a:b], f"config3 request {i} alone vs batch of 16 (lse)")
+
+
+def test_config4_mixed_batch(oracle):
+    work = wl.config4_mixed()
+    dev = Device(work)
+    mixed, full = work.batches["mixed"], work.batches["full"]
+    o_m, l_m = dev.run(mixed)
+    rows = np.concatenate([sample_rows(wl.sub_batch(mixed, work.prompts, 16, [0]), 40, seed=4),
+                           np.arange(3700, mixed.num_q_tokens)])
+    ro, rl = oracle_rows(oracle, work, mixed, rows)
+    assert_close_to_oracle(o_m, l_m, ro, rl, rows=rows, what="config4 mixed batch")
+    o_f, l_f = dev.run(full)
+    _check_pairs(mixed, o_m, l_m, full, o_f, l_f, [(i + 1, i) for i in range(7)], "config4")
+    # the full 3700-token request in the mixed batch equals itself alone
+    one = wl.sub_batch(mixed, work.prompts, 16, [0])
+    o1, l1 = dev.run(one)
+    assert_bits_equal(o1, o_m[:3700], "config4 full request alone vs mixed")
+    assert_bits_equal(l1, l_m[:3700], "config4 full request alone vs mixed (lse)")
+
+
+@pytest.fixture(scope="module")
+def config5():
+    return wl.config5_long_fp8()
+
+
+def test_config5_long_fp8_parity(oracle, config5):
+    work = config5
+    dev = Device(work)
+    for name in ("prefill_8192", "extend"):
+        b = work.batches[name]
+        o, l = dev.run(b, cap=256 << 20)
+        rows = sample_rows(b, 6, seed=5)
+        ro, rl = oracle_rows(oracle, work, b, rows)
+        assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"config5 {name}")
+
+
+def test_config5_extend_matches_32k_prefill(config5):
+    work = config5
+    dev = Device(work)
+    ext, full = work.batches["extend"], work.batches["prefill_32768"]
+    o_e, l_e = dev.run(ext, cap=256 << 20)
+    o_f, l_f = dev.run(full, cap=256 << 20)
+    _check_pairs(ext, o_e, l_e, full, o_f, l_f, [(0, 0)], "config5 extend vs 32k prefill")
+
+
+def test_config5_workspace_cap_does_not_change_bits(config5):
+    work = config5
+    dev = Device(work)
+    b = work.batches["prefill_8192"]
+    p_small = dev.plan(b, cap=32 << 20)
+    p_big = dev.plan(b, cap=0)
+    say(f"passes: cap 32 MiB -> {p_small.info.num_passes}, no cap -> {p_big.info.num_passes}")
+    assert p_small.info.num_passes > p_big.info.num_passes == 1
+    assert p_small.workspace_bytes <= 32 << 20
+    o1, l1 = dev.run(b, plan=p_small)
+    o2, l2 = dev.run(b, plan=p_big)
+    assert_bits_equal(o1, o2, "config5 8k: cap 32 MiB vs unbounded")
+    assert_bits_equal(l1, l2, "config5 8k: cap 32 MiB vs unbounded (lse)")

@@ -1,0 +1,268 @@
+"""CPU tests of the host planner and the C ABI's argument checks (no GPU, no kernel launch).
+
+Like the pages' host-plan test suite (sglang PR #46351, "Tests"), these check the work list
+itself: every (row, head, key <= p) is covered exactly once per split, each row's split count
+is a function of its position only, the workspace has a closed form and stays under the cap,
+and malformed input is rejected with a status before anything is launched.
+"""
+import ctypes
+import json
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import workloads as wl
+from dpp_header import parse
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def dpp():
+    import deterministic_paged_prefill_amd as dpp
+    if not os.path.exists(dpp.LIB_PATH):
+        from deterministic_paged_prefill_amd import build
+        build.build()
+    dpp.library()
+    return dpp
+
+
+def _align(x, a=256):
+    return (x + a - 1) // a * a
+
+
+def test_library_exports_every_declared_symbol(dpp):
+    header = open(os.path.join(ROOT, "include", "dpp.h")).read()
+    declared = set(re.findall(r"\b(dpp_[a-z_]+)\s*\(", header))
+    out = subprocess.run(["nm", "-D", "--defined-only", dpp.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = {line.split()[-1] for line in out.splitlines() if " T " in line}
+    assert declared, "no declarations parsed"
+    assert declared <= exported, declared - exported
+    assert declared == set(dpp.EXPORTS)
+    assert dpp.library().dpp_abi_version() == 1
+
+
+def _plan(dpp, batch, hq=32, hkv=8, d=128, page=16, cap=0, **kw):
+    return dpp.plan(hq, hkv, d, page, batch.qo_indptr, batch.kv_indptr,
+                    batch.kv_last_page_len, workspace_cap=cap, **kw)
+
+
+def _specs_batch(specs, page=16, g=4):
+    """A batch from (kv_len, qo_len) pairs without drawing data (page ids are arbitrary)."""
+    qo, kvp, last = [0], [0], []
+    for kv, qlen in specs:
+        npg = -(-kv // page)
+        qo.append(qo[-1] + qlen)
+        kvp.append(kvp[-1] + npg)
+        last.append(kv - (npg - 1) * page if npg else 0)
+
+    class B:
+        pass
+    b = B()
+    b.qo_indptr = np.array(qo, np.int32)
+    b.kv_indptr = np.array(kvp, np.int32)
+    b.kv_last_page_len = np.array(last, np.int32)
+    return b
+
+
+def _coverage(parsed, g, hkv=8):
+    """Map (request, packed row, split) -> set of KV tiles visited; check exactly-once."""
+    seen = {}
+    for it in parsed.items:
+        r, rs, s, S, kb, ke, slot, _ = (int(x) for x in it)
+        q_start, qo_len, page_start, kv_len = parsed.requests[r]
+        rows = min(128, qo_len * g - rs)
+        for lr in range(rows):
+            key = (r, rs + lr, s)
+            assert key not in seen, f"row {key} covered twice"
+            seen[key] = (kb, ke)
+    return seen
+
+
+@pytest.mark.parametrize("specs", [
+    [(67, 67)], [(67, 3)], [(1028, 1028)] * 3, [(1025, 1), (1028, 4), (1026, 2)],
+    [(3700, 3700), (3701, 1), (3702, 2), (3704, 4), (3706, 6), (3737, 37), (3764, 64), (4000, 300)],
+    [(9000, 9000)], [(8192, 100), (5000, 0), (4097, 4097)], [(1, 1), (0, 0), (2, 1)]])
+def test_every_key_covered_once_per_split(dpp, specs):
+    g = 4
+    b = _specs_batch(specs)
+    p = _plan(dpp, b)
+    parsed = parse(p.header())
+    cov = _coverage(parsed, g)
+    expected = set()
+    for r, (kv, qlen) in enumerate(specs):
+        for R in range(qlen * g):
+            pos = kv - qlen + R // g
+            n_splits = pos // 4096 + 1
+            for s in range(n_splits):
+                expected.add((r, R, s))
+                kb, ke = cov[(r, R, s)]
+                # the item visits every tile holding keys s*4096 .. min(p, split end)
+                assert kb == s * 64
+                assert ke * 64 > min(pos, (s + 1) * 4096 - 1)
+                assert ke <= (s + 1) * 64
+    # rows may ride along in items of splits they do not need (tile-mates' splits); the
+    # kernel skips their writes. Every needed (row, split) is present:
+    assert expected <= set(cov)
+
+
+def test_row_split_count_depends_only_on_position(dpp):
+    """A request's items (tile geometry, KV ranges) are identical alone and in any batch."""
+    alone = _specs_batch([(5000, 300)])
+    mixed = _specs_batch([(100, 100), (5000, 300), (9000, 1), (4096, 4096)])
+    a = parse(_plan(dpp, alone).header())
+    m = parse(_plan(dpp, mixed).header())
+    key = lambda it: (int(it[1]), int(it[2]), int(it[3]), int(it[4]), int(it[5]))
+    ia = sorted(key(it) for it in a.items if it[0] == 0)
+    im = sorted(key(it) for it in m.items if it[0] == 1)
+    assert ia == im
+
+
+def test_workspace_closed_form_single_pass(dpp):
+    specs = [(9000, 9000), (5000, 40), (100, 100)]
+    b = _specs_batch(specs)
+    p = _plan(dpp, b)
+    parsed = parse(p.header())
+    slots = 0
+    ntile = 0
+    for kv, qlen in specs:
+        for rs in range(0, qlen * 4, 128):
+            rows = min(128, qlen * 4 - rs)
+            pmax = kv - qlen + (rs + rows - 1) // 4
+            S = pmax // 4096 + 1
+            ntile += 1
+            if S > 1:
+                slots += S * 8 * 128
+    words = 16 + 4 * len(specs) + 8 * len(parsed.items) + 4 * len(parsed.merges)
+    hdr = _align(words * 4)
+    assert p.info.header_bytes == hdr
+    assert p.info.max_partial_slots == slots
+    assert p.workspace_bytes == hdr + _align(slots * 128 * 4) + _align(slots * 4)
+    assert p.info.num_passes == 1
+
+
+@pytest.mark.parametrize("cap_mib", [8, 16, 64])
+def test_cap_bounds_workspace_and_adds_passes(dpp, cap_mib):
+    b = _specs_batch([(32768, 32768)])
+    cap = cap_mib << 20
+    unbounded = dpp.plan(24, 4, 256, 16, b.qo_indptr, b.kv_indptr, b.kv_last_page_len,
+                         kv_dtype="fp8_e4m3", k_scale=1 / 32, v_scale=1 / 32, workspace_cap=0)
+    p = dpp.plan(24, 4, 256, 16, b.qo_indptr, b.kv_indptr, b.kv_last_page_len,
+                 kv_dtype="fp8_e4m3", k_scale=1 / 32, v_scale=1 / 32, workspace_cap=cap)
+    assert p.workspace_bytes <= cap
+    assert p.info.num_passes > 1
+    assert unbounded.info.num_passes == 1
+    assert unbounded.workspace_bytes > 3 << 30  # ~3.5 GB of partials without a cap
+    # same work, only cut into passes
+    key = lambda it: tuple(int(x) for x in it[:6])
+    assert sorted(map(key, parse(p.header()).items)) == sorted(map(key, parse(unbounded.header()).items))
+
+
+def test_zero_length_request_gets_no_rows(dpp):
+    b = _specs_batch([(50, 0), (50, 5), (0, 0)])
+    parsed = parse(_plan(dpp, b).header())
+    assert set(int(r) for r in parsed.items[:, 0]) == {1}
+    assert parsed.requests[0][1] == 0 and parsed.requests[2][3] == 0
+
+
+def test_p2_split_workspace_figures():
+    """The pages' split-buffer numbers follow from q tiles x fixed 4096-token splits.
+
+    Pinned against the figures the page prints: 1,536 work items and 2,415,919,104 bytes for
+    an 8,192-token prefill at 24/4/256 with cta_tile_q 64, and the ~7,275-token prompt at
+    which a fixed 2 GiB buffer first overflows. Our planner uses the same item structure
+    (one item per q tile per split), but bounds the partials by passes.
+    """
+    with open(os.path.join(ROOT, "tests", "golden", "split_workspace_p2.json")) as f:
+        gold = json.load(f)
+    s = gold["shape"]
+    g = s["num_qo_heads"] // s["num_kv_heads"]
+
+    def items(n):
+        return -(-n * g // s["cta_tile_q"]) * -(-n // s["split_tokens"])
+
+    def buffer_bytes(n):
+        return s["num_qo_heads"] * items(n) * s["cta_tile_q"] * s["head_dim"] * 4
+
+    assert items(gold["prefill_tokens"]) == gold["work_items"]
+    assert buffer_bytes(gold["prefill_tokens"]) == gold["buffer_bytes"]
+    first = next(n for n in range(1, 10000) if buffer_bytes(n) > gold["fixed_workspace_bytes"])
+    assert first == gold["first_overflowing_prompt_tokens_approx"]
+
+
+@pytest.mark.parametrize("mutate,status", [
+    (lambda q, k, l: q.__setitem__(1, q[2] + 1), "DPP_ERR_INVALID"),    # non-monotone qo_indptr
+    (lambda q, k, l: q.__setitem__(0, 1), "DPP_ERR_INVALID"),            # qo_indptr[0] != 0
+    (lambda q, k, l: k.__setitem__(1, -1), "DPP_ERR_INVALID"),           # negative page count
+    (lambda q, k, l: l.__setitem__(0, 0), "DPP_ERR_SHAPE"),              # last page length 0
+    (lambda q, k, l: l.__setitem__(0, 17), "DPP_ERR_SHAPE"),             # last page length > page
+    (lambda q, k, l: q.__setitem__(slice(1, None), q[1:] + 100), "DPP_ERR_SHAPE"),  # qo_len > kv_len
+])
+def test_malformed_batches_are_rejected(dpp, mutate, status):
+    b = _specs_batch([(67, 3), (40, 40)])
+    q, k, l = b.qo_indptr.copy(), b.kv_indptr.copy(), b.kv_last_page_len.copy()
+    mutate(q, k, l)
+    with pytest.raises(dpp.DppValueError, match=status):
+        dpp.plan(32, 8, 128, 16, q, k, l)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=64), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=30, num_kv_heads=8, head_dim=128), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=0), "DPP_ERR_UNSUPPORTED"),
+])
+def test_unsupported_configs(dpp, args, status):
+    b = _specs_batch([(67, 3)])
+    kw = dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=16)
+    kw.update(args)
+    with pytest.raises(dpp.DppValueError, match=status):
+        dpp.plan(kw["num_qo_heads"], kw["num_kv_heads"], kw["head_dim"], kw["page_size"],
+                 b.qo_indptr, b.kv_indptr, b.kv_last_page_len)
+
+
+def test_cap_below_one_tile_is_rejected(dpp):
+    b = _specs_batch([(9000, 9000)])
+    with pytest.raises(dpp.DppValueError, match="DPP_ERR_WORKSPACE"):
+        _plan(dpp, b, cap=1 << 20)
+
+
+def test_run_rejects_bad_shapes_before_any_launch(dpp):
+    """dpp_run's checks happen on the host before any HIP call (exercised here without a GPU)."""
+    lib = dpp.library()
+    b = _specs_batch([(67, 3)])
+    p = _plan(dpp, b)
+    fake = 1 << 20  # never dereferenced: every call below fails its host-side checks
+    ws = p.workspace_bytes
+    st = lib.dpp_run(p._h, fake, 4, fake, fake, 64, fake, fake, fake, fake, ws, None)
+    assert st == dpp.DPP_ERR_SHAPE and b"q has 4 rows" in lib.dpp_last_error()
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake, ws - 1, None)
+    assert st == dpp.DPP_ERR_WORKSPACE
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake + 16, ws, None)
+    assert st == dpp.DPP_ERR_WORKSPACE  # misaligned workspace
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, None, ws, None)
+    assert st == dpp.DPP_ERR_WORKSPACE
+    st = lib.dpp_merge_states(fake, fake, 1, 0, 1, 128, fake, fake, None)
+    assert st == dpp.DPP_ERR_INVALID
+    st = lib.dpp_merge_states(fake, fake, 1, 2, 1, 130, fake, fake, None)
+    assert st == dpp.DPP_ERR_UNSUPPORTED
+
+
+def test_null_arguments(dpp):
+    lib = dpp.library()
+    assert lib.dpp_plan_create(None, 0, None, None, None, 0, None) == dpp.DPP_ERR_INVALID
+    assert lib.dpp_plan_workspace_bytes(None) == 0
+    lib.dpp_plan_destroy(None)
+
+
+def test_workload_batches_plan(dpp):
+    """Every configuration's batches plan without error (shapes only; no data drawn here)."""
+    for specs in ([(1028, 1028)] * 16, [(1024 + t, t) for t in (1, 2, 3, 4)] * 4):
+        p = _plan(dpp, _specs_batch(specs))
+        assert p.info.num_prefill_items > 0
+    work = wl.config1_single_extend()
+    p = _plan(dpp, work.batches["cached"])
+    assert p.info.total_q_rows == 3
