@@ -1,0 +1,311 @@
+#!/usr/bin/env python3
+"""Benchmark of batch-invariant paged-KV causal GQA prefill attention on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Prints ONE JSON line. A step is one pass of the whole attention path over one batch (the
+prefill kernel, plus the merge kernel when rows span several 4096-token splits); the plan and
+its work-list upload are made once per batch shape, outside the timed region, as a model
+reuses them for every layer (their host / upload times are reported separately).
+
+value     extend KV GB/s: 16 requests, each extending 1-4 tokens behind a 1024-token prefix
+          (32 q / 8 kv heads, head_dim 128, bf16, page 16). Every request owns a private copy
+          of its prefix pages and 8 such pools are rotated across steps (> 512 MB), so the
+          256 MB Infinity Cache cannot serve the KV: logical KV bytes / step time.
+prefill   cold 16 x 1028-token causal prefill, same shapes: causal FLOPs / step time.
+roofline  the extend kernel against HBM (8 TB/s); prefill's own against bf16 MFMA peak.
+cpu_baseline  the fp64 CPU oracle on the same extend batch, repeated for ~10 s.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+BF16_MFMA_PEAK_TFLOPS = 2516.6  # 256 CU x 2.4 GHz x 4096 dense bf16 FLOP/clk/CU
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "extend_16x1-4_behind_1024_counters.json")
+KERNEL_SOURCES = ["deterministic_paged_prefill_amd/csrc/prefill.hip",
+                  "deterministic_paged_prefill_amd/csrc/dpp_internal.h"]
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def causal_flops(batch, hq: int, d: int) -> float:
+    """4 * d * Hq * sum over query rows of (p + 1) keys: QK^T and PV, causal work only."""
+    total = 0
+    for r in batch.requests:
+        a = r.kv_len - r.qo_len  # position of the first query row
+        # sum_{p=a}^{kv_len-1} (p + 1)
+        total += (r.kv_len * (r.kv_len + 1) - a * (a + 1)) // 2
+    return 4.0 * d * hq * total
+
+
+def kv_bytes(batch, hkv: int, d: int, elem: int) -> int:
+    """Logical KV bytes: every request's K and V rows read once."""
+    return sum(r.kv_len for r in batch.requests) * hkv * d * 2 * elem
+
+
+class Runner:
+    """Pre-resolved dpp_run arguments so the timed loop is one C call per step."""
+
+    def __init__(self, work, batch, replicas: int = 1, cap: int = 256 << 20):
+        import torch
+
+        import deterministic_paged_prefill_amd as dpp
+        self.dpp = dpp
+        self.lib = dpp.library()
+        self.work = work
+        self.batch = batch
+        t0 = time.perf_counter()
+        self.plan = dpp.plan(work.num_qo_heads, work.num_kv_heads, work.head_dim, work.page_size,
+                             batch.qo_indptr, batch.kv_indptr, batch.kv_last_page_len,
+                             kv_dtype=work.kv_dtype, k_scale=work.k_scale, v_scale=work.v_scale,
+                             workspace_cap=cap)
+        self.plan_us = (time.perf_counter() - t0) * 1e6
+        dev = torch.device("cuda")
+        P = work.num_pages
+        # replica i: the whole pool copied to pages [i*P, (i+1)*P), page ids shifted by i*P
+        self.k = work.k_pool.to(dev).repeat(replicas, 1, 1, 1).contiguous()
+        self.v = work.v_pool.to(dev).repeat(replicas, 1, 1, 1).contiguous()
+        base = torch.from_numpy(batch.kv_indices).to(dev)
+        self.kvi = [(base + i * P).contiguous() for i in range(replicas)]
+        self.q = batch.q.to(dev)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty((self.q.shape[0], work.num_qo_heads), dtype=torch.float32, device=dev)
+        self.ws = self.plan.new_workspace(dev)
+        self.stream = torch.cuda.current_stream()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        self.plan.upload(self.ws, self.stream)
+        torch.cuda.synchronize()
+        self.upload_us = (time.perf_counter() - t0) * 1e6
+        self.replicas = replicas
+        self.args = [(self.plan._h, self.q.data_ptr(), self.q.shape[0], self.k.data_ptr(),
+                      self.v.data_ptr(), self.k.shape[0], kvi.data_ptr(), self.o.data_ptr(),
+                      self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+                      dpp.RUN_REUSE_UPLOAD, self.stream.cuda_stream) for kvi in self.kvi]
+
+    def step(self, i: int) -> None:
+        st = self.lib.dpp_run(*self.args[i % self.replicas])
+        if st != 0:
+            self.dpp._check(st)
+
+    def timed(self, steps: int, warmup: int):
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record(self.stream)
+        for i in range(steps):
+            self.step(warmup + i)
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        wall_ms = (time.perf_counter() - t0) * 1e3
+        return start.elapsed_time(end) / steps, wall_ms / steps
+
+    def outputs(self, replica: int = 0):
+        import torch
+        self.step(replica)
+        torch.cuda.synchronize()
+        return self.o.cpu(), self.lse.cpu()
+
+
+def traffic_from_profile(launch_bytes: float):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was taken on
+    the current kernel source (else None)."""
+    try:
+        with open(PROFILE_COUNTERS) as f:
+            prof = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if prof.get("kernel_source_sha256_16") != kernel_hash():
+        return None
+    scale = prof.get("copy_calibration_factor", 1.0)
+    return (prof["fetch_kib_per_dispatch"] + prof["write_kib_per_dispatch"]) * 1024.0 * scale
+
+
+def cpu_baseline(work, batch, budget_s: float):
+    import oracle
+    oracle.build(force=False)
+    kw = work.oracle_kwargs(batch)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.paged_prefill(**kw)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s:
+            break
+    gb = kv_bytes(batch, work.num_kv_heads, work.head_dim, 2) * reps / 1e9
+    return {"value": round(gb / el, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"the whole extend batch ({batch.num_q_tokens} query tokens x "
+                      f"{work.num_qo_heads} heads over 1025-1028 keys each), fp64 C + OpenMP, "
+                      f"{reps} repetitions in {el:.1f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--replicas", type=int, default=8, help="rotated KV pools for the extend batch")
+    ap.add_argument("--cpu-budget-s", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only", choices=["extend", "prefill", "copy"], default=None,
+                    help="run one leg only and print its timing (for profiler runs)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark measures one GPU: the attention path is built "
+                                   "and measured on a single MI355X (see DESIGN.md for how it "
+                                   "would shard); run with --gpus 1"}))
+        return 2
+
+    import numpy as np
+    import torch
+
+    import workloads as wl
+    if not torch.cuda.is_available():
+        log("no GPU visible")
+        return 1
+
+    if args.only == "copy":
+        # calibration for the HBM byte counters: one device copy of exactly 512 MiB
+        n = 512 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n} bytes x3")
+        return 0
+
+    hq, hkv, d = 32, 8, 128
+    result = {}
+
+    # ---------------------------------------------------------------- extend (value)
+    if args.only in (None, "extend"):
+        log("building extend workload (distinct pages)")
+        work = wl.config2_extend_batch(layout="distinct")
+        cached, full = work.batches["cached"], work.batches["full"]
+        run = Runner(work, cached, replicas=args.replicas)
+        # the metric's bit-exactness clause: cached rows vs the same rows of a full prefill
+        o_c, l_c = run.outputs(0)
+        fr = Runner(work, full, replicas=1)
+        o_f, l_f = fr.outputs(0)
+        max_diff = 0.0
+        for r in range(cached.batch_size):
+            ia, ib = wl.matching_rows(cached, r, full, r)
+            max_diff = max(max_diff, float((o_c[ia].float() - o_f[ib].float()).abs().max()),
+                           float((l_c[ia] - l_f[ib]).abs().max()))
+        assert np.isfinite(o_c.float().numpy()).all()
+        del fr
+        log(f"cached-vs-full max|diff| = {max_diff}")
+        ms, wall = run.timed(args.steps, args.warmup)
+        if args.only == "extend":
+            log(f"extend: {ms * 1e3:.2f} us/step (wall {wall * 1e3:.2f} us)")
+            return 0
+        nbytes = kv_bytes(cached, hkv, d, 2)
+        io_bytes = (2 * cached.num_q_tokens * hq * d * 2 + cached.num_q_tokens * hq * 4
+                    + cached.kv_indices.size * 4)
+        alg = nbytes + io_bytes
+        achieved = alg / (ms * 1e-3) / 1e9
+        result["extend"] = dict(ms=ms, wall_ms=wall, kv_bytes=nbytes, alg_bytes=alg, gbps=nbytes / (ms * 1e-3) / 1e9,
+                                achieved=achieved, plan_us=run.plan_us, upload_us=run.upload_us,
+                                max_diff=max_diff, work=work, batch=cached,
+                                items=run.plan.info.num_prefill_items)
+        # radix layout (prefix pages physically shared): logical bytes over a cache-served read
+        work_r = wl.config2_extend_batch(layout="radix")
+        rr = Runner(work_r, work_r.batches["cached"], replicas=1)
+        ms_r, _ = rr.timed(args.steps, args.warmup)
+        result["extend"]["radix_logical_gbps"] = kv_bytes(work_r.batches["cached"], hkv, d, 2) / (ms_r * 1e-3) / 1e9
+        result["extend"]["radix_ms"] = ms_r
+        del rr, run
+
+    # ---------------------------------------------------------------- cold prefill
+    if args.only in (None, "prefill") and not args.no_prefill:
+        log("building cold prefill workload")
+        work_p = wl.config3_cold_prefill()
+        bp = work_p.batches["full"]
+        pr = Runner(work_p, bp, replicas=1)
+        ms_p, wall_p = pr.timed(max(10, args.steps // 4), max(3, args.warmup // 4))
+        if args.only == "prefill":
+            log(f"prefill: {ms_p * 1e3:.2f} us/step")
+            return 0
+        fl = causal_flops(bp, hq, d)
+        result["prefill"] = dict(ms=ms_p, flops=fl, tflops=fl / (ms_p * 1e-3) / 1e12,
+                                 plan_us=pr.plan_us, items=pr.plan.info.num_prefill_items)
+        del pr
+
+    ext = result["extend"]
+    traffic = traffic_from_profile(ext["alg_bytes"])
+    line = {
+        "metric": "prefill attn TFLOP/s + extend KV GB/s (1 GPU); cached-vs-full max|diff|=0",
+        "value": round(ext["gbps"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ext["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "extend batch: 16 requests x 1-4 new tokens (uniform) behind a "
+                               "1024-token prefix, 32 q / 8 kv heads, head_dim 128, bf16, page 16, "
+                               f"distinct prefix pages, {args.replicas} rotated pools",
+                   "kv_bytes_per_step": ext["kv_bytes"],
+                   "query_tokens": int(ext["batch"].num_q_tokens),
+                   "parallelism": "single GPU"},
+        "cached_vs_full_max_abs_diff": ext["max_diff"],
+        "roofline": {"bound": "hbm", "achieved": round(ext["achieved"], 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(ext["achieved"] / HBM_PEAK_GBPS, 4),
+                     "traffic": None if traffic is None else round(traffic)},
+        "extend_detail": {"us_per_step": round(ext["ms"] * 1e3, 2),
+                          "host_wall_us_per_step": round(ext["wall_ms"] * 1e3, 2),
+                          "algorithmic_bytes_per_launch": ext["alg_bytes"],
+                          "work_items": ext["items"], "plan_us": round(ext["plan_us"], 1),
+                          "upload_us": round(ext["upload_us"], 1),
+                          "radix_layout_logical_gbps": round(ext["radix_logical_gbps"], 1),
+                          "radix_layout_us_per_step": round(ext["radix_ms"] * 1e3, 2)},
+        "kernel_source_sha256_16": kernel_hash(),
+    }
+    if "prefill" in result:
+        p = result["prefill"]
+        line["prefill"] = {"workload": "cold causal prefill, 16 x 1028 tokens, 32/8/128 bf16, page 16",
+                           "tflops": round(p["tflops"], 2), "ms_per_step": round(p["ms"], 5),
+                           "causal_flops": p["flops"], "work_items": p["items"],
+                           "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2),
+                                        "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                                        "frac": round(p["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle")
+        line["cpu_baseline"] = cpu_baseline(ext["work"], ext["batch"], args.cpu_budget_s)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

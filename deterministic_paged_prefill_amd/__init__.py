@@ -30,6 +30,7 @@ DEFAULT_WORKSPACE_CAP = 256 << 20
 BLOCK_M, BLOCK_N, SPLIT_TOKENS = 128, 64, 4096
 
 DPP_OK, DPP_ERR_INVALID, DPP_ERR_SHAPE, DPP_ERR_UNSUPPORTED, DPP_ERR_WORKSPACE, DPP_ERR_HIP = range(6)
+RUN_REUSE_UPLOAD = 1
 KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -78,7 +79,7 @@ class PlanInfo:
 
 _lib = None
 EXPORTS = ("dpp_plan_create", "dpp_plan_workspace_bytes", "dpp_plan_get_info", "dpp_plan_header",
-           "dpp_plan_destroy", "dpp_run", "dpp_merge_states", "dpp_last_error",
+           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_merge_states", "dpp_last_error",
            "dpp_status_string", "dpp_abi_version")
 
 
@@ -100,10 +101,12 @@ def library():
     lib.dpp_plan_get_info.argtypes = [vp, ctypes.POINTER(_PlanInfo)]
     lib.dpp_plan_header.restype = ctypes.c_int
     lib.dpp_plan_header.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(sz)]
+    lib.dpp_plan_upload.restype = ctypes.c_int
+    lib.dpp_plan_upload.argtypes = [vp, vp, sz, vp]
     lib.dpp_plan_destroy.restype = None
     lib.dpp_plan_destroy.argtypes = [vp]
     lib.dpp_run.restype = ctypes.c_int
-    lib.dpp_run.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, sz, vp]
+    lib.dpp_run.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, sz, ctypes.c_uint32, vp]
     lib.dpp_merge_states.restype = ctypes.c_int
     lib.dpp_merge_states.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp]
     lib.dpp_last_error.restype = ctypes.c_char_p
@@ -170,9 +173,19 @@ class Plan:
         import torch
         return torch.empty(max(self.workspace_bytes, 256), dtype=torch.uint8, device=device)
 
+    def upload(self, workspace, stream=None) -> None:
+        """Copy the work list into ``workspace`` once; later run(..., reuse_upload=True) skip it."""
+        _check(library().dpp_plan_upload(self._h, workspace.data_ptr(),
+                                         workspace.numel() * workspace.element_size(),
+                                         _stream_handle(stream)))
+        self._ran = True
+
     def run(self, q, k_pool, v_pool, kv_indices, out=None, lse=None, workspace=None,
-            stream=None):
-        """Attention of the planned batch. Returns (o bf16 [rows, Hq, D], lse fp32 [rows, Hq])."""
+            stream=None, reuse_upload: bool = False):
+        """Attention of the planned batch. Returns (o bf16 [rows, Hq, D], lse fp32 [rows, Hq]).
+
+        ``reuse_upload=True`` requires an earlier upload()/run() of this plan into the same
+        ``workspace`` (nothing else written to its head since)."""
         import torch
         c = self.cfg
         rows = q.shape[0]
@@ -205,11 +218,14 @@ class Plan:
         if tuple(lse.shape) != (rows, c.num_qo_heads) or lse.dtype != torch.float32 or not lse.is_contiguous():
             raise ValueError("lse must be a contiguous fp32 tensor [rows, num_qo_heads]")
         if workspace is None:
+            if reuse_upload:
+                raise ValueError("reuse_upload needs the workspace the plan was uploaded to")
             workspace = self.new_workspace(q.device)
         status = library().dpp_run(self._h, q.data_ptr(), rows, k_pool.data_ptr(), v_pool.data_ptr(),
                                    k_pool.shape[0], kv_indices.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(),
+                                   RUN_REUSE_UPLOAD if reuse_upload else 0,
                                    _stream_handle(stream))
         _check(status)
         self._ran = True

@@ -23,36 +23,25 @@ bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 }  // namespace
 
+
 extern "C" void dpp_plan_destroy(dpp_plan* plan) {
   if (!plan) return;
   if (plan->pinned) (void)hipHostFree(plan->pinned);
   delete plan;
 }
 
-extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows,
-                              const void* k_pool, const void* v_pool, int64_t num_pages,
-                              const int32_t* kv_indices, void* o, float* lse, void* workspace,
-                              size_t workspace_bytes, void* stream_ptr) {
-  if (!plan) return fail(DPP_ERR_INVALID, "dpp_run: null plan");
-  if (q_rows != plan->total_q_rows)
-    return fail(DPP_ERR_SHAPE, "q has " + std::to_string(q_rows) + " rows but qo_indptr[-1] is " +
-                                   std::to_string(plan->total_q_rows));
-  if (num_pages < 0) return fail(DPP_ERR_INVALID, "dpp_run: negative num_pages");
-  if (!workspace) return fail(DPP_ERR_WORKSPACE, "dpp_run: null workspace");
-  if (!aligned(workspace, 256)) return fail(DPP_ERR_WORKSPACE, "dpp_run: workspace not 256-byte aligned");
+namespace {
+
+dpp_status check_workspace(const dpp_plan* plan, const void* workspace, size_t workspace_bytes) {
+  if (!workspace) return fail(DPP_ERR_WORKSPACE, "null workspace");
+  if (!aligned(workspace, 256)) return fail(DPP_ERR_WORKSPACE, "workspace not 256-byte aligned");
   if (workspace_bytes < plan->workspace_bytes)
     return fail(DPP_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
                                        " B, the plan needs " + std::to_string(plan->workspace_bytes) + " B");
-  if (plan->total_q_rows > 0 && (!q || !o || !lse))
-    return fail(DPP_ERR_INVALID, "dpp_run: null q, o or lse");
-  if (plan->num_items > 0 && (!k_pool || !v_pool || !kv_indices))
-    return fail(DPP_ERR_INVALID, "dpp_run: null k_pool, v_pool or kv_indices");
-  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(lse, 4) || !aligned(kv_indices, 4))
-    return fail(DPP_ERR_INVALID, "dpp_run: q/o/k_pool/v_pool must be 16-byte aligned");
-  hipStream_t stream = (hipStream_t)stream_ptr;
-  if (plan->num_items == 0) return DPP_OK;
+  return DPP_OK;
+}
 
+dpp_status enqueue_upload(const dpp_plan* plan, void* workspace, hipStream_t stream) {
   const size_t hbytes = plan->header.size() * sizeof(int32_t);
   {
     std::lock_guard<std::mutex> lock(plan->pinned_mu);
@@ -66,6 +55,45 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   }
   hipError_t e = hipMemcpyAsync(workspace, plan->pinned, hbytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  return DPP_OK;
+}
+
+}  // namespace
+
+extern "C" dpp_status dpp_plan_upload(const dpp_plan* plan, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  if (!plan) return fail(DPP_ERR_INVALID, "dpp_plan_upload: null plan");
+  dpp_status st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != DPP_OK) return st;
+  return enqueue_upload(plan, workspace, (hipStream_t)stream);
+}
+
+extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows,
+                              const void* k_pool, const void* v_pool, int64_t num_pages,
+                              const int32_t* kv_indices, void* o, float* lse, void* workspace,
+                              size_t workspace_bytes, uint32_t flags, void* stream_ptr) {
+  if (!plan) return fail(DPP_ERR_INVALID, "dpp_run: null plan");
+  if (q_rows != plan->total_q_rows)
+    return fail(DPP_ERR_SHAPE, "q has " + std::to_string(q_rows) + " rows but qo_indptr[-1] is " +
+                                   std::to_string(plan->total_q_rows));
+  if (num_pages < 0) return fail(DPP_ERR_INVALID, "dpp_run: negative num_pages");
+  if (flags & ~DPP_RUN_REUSE_UPLOAD) return fail(DPP_ERR_INVALID, "dpp_run: unknown flags");
+  dpp_status st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != DPP_OK) return st;
+  if (plan->total_q_rows > 0 && (!q || !o || !lse))
+    return fail(DPP_ERR_INVALID, "dpp_run: null q, o or lse");
+  if (plan->num_items > 0 && (!k_pool || !v_pool || !kv_indices))
+    return fail(DPP_ERR_INVALID, "dpp_run: null k_pool, v_pool or kv_indices");
+  if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(lse, 4) || !aligned(kv_indices, 4))
+    return fail(DPP_ERR_INVALID, "dpp_run: q/o/k_pool/v_pool must be 16-byte aligned");
+  hipStream_t stream = (hipStream_t)stream_ptr;
+  if (plan->num_items == 0) return DPP_OK;
+  if (!(flags & DPP_RUN_REUSE_UPLOAD)) {
+    st = enqueue_upload(plan, workspace, stream);
+    if (st != DPP_OK) return st;
+  }
+  hipError_t e;
 
   char* ws = (char*)workspace;
   PrefillArgs a{};
@@ -79,6 +107,7 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   a.part_o = (float*)(ws + plan->partial_o_offset);
   a.part_lse2 = (float*)(ws + plan->partial_lse_offset);
   a.num_pages = num_pages;
+  a.plan_id = plan->plan_id;
   a.num_qo_heads = plan->cfg.num_qo_heads;
   a.num_kv_heads = plan->cfg.num_kv_heads;
   a.group = plan->group;
@@ -96,6 +125,7 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   m.lse = lse;
   m.num_qo_heads = plan->cfg.num_qo_heads;
   m.group = plan->group;
+  m.plan_id = plan->plan_id;
 
   const int passes = (int)plan->item_pass.size() - 1;
   for (int p = 0; p < passes; ++p) {

@@ -81,7 +81,8 @@ struct HeaderPreamble {
   int32_t request_offset;  // word offsets from the start of the header
   int32_t item_offset;
   int32_t merge_offset;
-  int32_t reserved[kHeaderWords - 7];
+  uint32_t plan_id;        // unique per plan; kernels refuse a header with another id
+  int32_t reserved[kHeaderWords - 8];
 };
 static_assert(sizeof(HeaderPreamble) == kHeaderWords * 4, "preamble size");
 
@@ -98,6 +99,7 @@ struct PrefillArgs {
   float* part_o;            // [slots, D]
   float* part_lse2;         // [slots] (base-2 log-sum-exp of the split)
   int64_t num_pages;
+  uint32_t plan_id;
   int32_t item_begin;       // first item of this pass
   int32_t num_items;        // items in this pass
   int32_t num_qo_heads;
@@ -116,6 +118,7 @@ struct MergeArgs {
   const float* part_lse2;
   void* o;
   float* lse;
+  uint32_t plan_id;
   int32_t merge_begin;
   int32_t num_merges;
   int32_t num_qo_heads;

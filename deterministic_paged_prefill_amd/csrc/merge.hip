@@ -68,6 +68,7 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
   constexpr int kTpr = D / 4;              // threads per row (4 columns each)
   constexpr int kRowsPerPass = kThreads / kTpr;
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
+  if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
   const MergeItem mi = reinterpret_cast<const MergeItem*>(a.header + pre->merge_offset)[a.merge_begin + blockIdx.x];
   const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[mi.request];
   const int kvh = blockIdx.y;

@@ -17,6 +17,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <atomic>
 #include <cmath>
 #include <cstring>
 #include <limits>
@@ -228,6 +229,14 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   pre.request_offset = kHeaderWords;
   pre.item_offset = kHeaderWords + 4 * batch_size;
   pre.merge_offset = pre.item_offset + 8 * (int32_t)n_items;
+  {
+    // ids differ between plans of one process; mixing in the address makes a header left
+    // behind by another process unlikely to match either
+    static std::atomic<uint32_t> counter{0x9E3779B9u};
+    uint32_t id = counter.fetch_add(0x61C88647u) ^ (uint32_t)(uintptr_t)plan.get();
+    pre.plan_id = id == 0 ? 1u : id;
+    plan->plan_id = pre.plan_id;
+  }
   std::memcpy(plan->header.data(), &pre, sizeof pre);
   if (batch_size > 0)
     std::memcpy(plan->header.data() + pre.request_offset, reqs.data(), reqs.size() * sizeof(RequestDesc));

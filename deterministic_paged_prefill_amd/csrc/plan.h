@@ -33,6 +33,7 @@ struct dpp_plan {
   size_t partial_lse_offset = 0;
   size_t workspace_bytes = 0;
   int32_t page_slots = 0;         // LDS page-id entries one item may need
+  uint32_t plan_id = 0;           // stamped into the work list
 
   // Pinned host copy of `header`, created on first dpp_run (plan creation stays HIP-free).
   mutable std::mutex pinned_mu;

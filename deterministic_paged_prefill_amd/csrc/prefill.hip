@@ -174,6 +174,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const int kvh = blockIdx.y;
 
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
+  if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
   const PrefillItem it =
       reinterpret_cast<const PrefillItem*>(a.header + pre->item_offset)[a.item_begin + blockIdx.x];
   const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[it.request];

@@ -126,9 +126,23 @@ dpp_status dpp_plan_get_info(const dpp_plan* plan, dpp_plan_info* info);
  * dpp_plan_destroy). Layout: int32 words; see the planner source for the record format. */
 dpp_status dpp_plan_header(const dpp_plan* plan, const void** data, size_t* bytes);
 
+/*
+ * Enqueue the copy of the plan's work list into the head of `workspace` on `stream`.
+ * dpp_run does this itself unless called with DPP_RUN_REUSE_UPLOAD; a caller that runs the
+ * same plan many times (every layer of a model on one batch) uploads once and passes the flag.
+ * The plan's id is stamped into the copy; kernels launched for another plan, or over a
+ * workspace whose head was overwritten, find a different id and write nothing.
+ * Errors: DPP_ERR_INVALID (null), DPP_ERR_WORKSPACE (size / alignment), DPP_ERR_HIP.
+ */
+dpp_status dpp_plan_upload(const dpp_plan* plan, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* Free a plan. The plan must outlive the stream work of every dpp_run that used it (the
  * upload of its work list reads the plan's pinned host buffer asynchronously). NULL is a no-op. */
 void dpp_plan_destroy(dpp_plan* plan);
+
+/* dpp_run flags */
+#define DPP_RUN_REUSE_UPLOAD 1u /* the workspace already holds this plan's work list */
 
 /*
  * Run the planned attention on `stream` (a hipStream_t; NULL = the null stream).
@@ -138,14 +152,18 @@ void dpp_plan_destroy(dpp_plan* plan);
  *   num_pages     pages in each pool; a page id outside [0, num_pages) reads as zeros
  *   workspace     device buffer of at least dpp_plan_workspace_bytes(plan) bytes, 256-byte
  *                 aligned; its contents are scratch (work list + split partials)
+ *   flags         0, or DPP_RUN_REUSE_UPLOAD when dpp_plan_upload (or an earlier dpp_run) has
+ *                 already put this plan's work list into this workspace on this stream
  *
- * Enqueues: one async copy of the work list into the workspace, then per pass one prefill
- * launch and (if some row spans several splits) one merge launch. Returns without waiting.
+ * Enqueues: the async copy of the work list into the workspace (unless reused), then per pass
+ * one prefill launch and (if some row spans several splits) one merge launch. Returns without
+ * waiting.
  * On DPP_ERR_SHAPE / DPP_ERR_WORKSPACE / DPP_ERR_UNSUPPORTED nothing is enqueued.
  */
 dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows, const void* k_pool,
                    const void* v_pool, int64_t num_pages, const int32_t* kv_indices, void* o,
-                   float* lse, void* workspace, size_t workspace_bytes, void* stream);
+                   float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
+                   void* stream);
 
 /*
  * Combine softmax partial states, the same device merge dpp_run uses for split rows.

@@ -237,13 +237,17 @@ def test_run_rejects_bad_shapes_before_any_launch(dpp):
     p = _plan(dpp, b)
     fake = 1 << 20  # never dereferenced: every call below fails its host-side checks
     ws = p.workspace_bytes
-    st = lib.dpp_run(p._h, fake, 4, fake, fake, 64, fake, fake, fake, fake, ws, None)
+    st = lib.dpp_run(p._h, fake, 4, fake, fake, 64, fake, fake, fake, fake, ws, 0, None)
     assert st == dpp.DPP_ERR_SHAPE and b"q has 4 rows" in lib.dpp_last_error()
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake, ws - 1, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake, ws - 1, 0, None)
     assert st == dpp.DPP_ERR_WORKSPACE
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake + 16, ws, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake + 16, ws, 0, None)
     assert st == dpp.DPP_ERR_WORKSPACE  # misaligned workspace
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, None, ws, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, None, ws, 0, None)
+    assert st == dpp.DPP_ERR_WORKSPACE
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake, ws, 4, None)
+    assert st == dpp.DPP_ERR_INVALID  # unknown flag
+    st = lib.dpp_plan_upload(p._h, fake + 16, ws, None)
     assert st == dpp.DPP_ERR_WORKSPACE
     st = lib.dpp_merge_states(fake, fake, 1, 0, 1, 128, fake, fake, None)
     assert st == dpp.DPP_ERR_INVALID
