@@ -22,12 +22,16 @@ from dataclasses import dataclass
 import numpy as np
 
 __all__ = ["plan", "Plan", "PlanInfo", "merge_states", "library", "LibraryNotBuilt",
-           "DppError", "DppValueError", "DEFAULT_WORKSPACE_CAP", "BLOCK_M", "BLOCK_N",
-           "SPLIT_TOKENS"]
+           "DppError", "DppValueError", "DEFAULT_WORKSPACE_CAP", "SPLIT_TOKENS", "tile_shape"]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdpp.so")
 DEFAULT_WORKSPACE_CAP = 256 << 20
-BLOCK_M, BLOCK_N, SPLIT_TOKENS = 128, 64, 4096
+SPLIT_TOKENS = 4096
+
+
+def tile_shape(head_dim: int) -> tuple:
+    """(packed query rows, keys) of one tile: constants of head_dim (see dpp_internal.h)."""
+    return (256, 64) if head_dim <= 128 else (128, 32)
 
 DPP_OK, DPP_ERR_INVALID, DPP_ERR_SHAPE, DPP_ERR_UNSUPPORTED, DPP_ERR_WORKSPACE, DPP_ERR_HIP = range(6)
 RUN_REUSE_UPLOAD = 1

@@ -126,6 +126,7 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   m.num_qo_heads = plan->cfg.num_qo_heads;
   m.group = plan->group;
   m.plan_id = plan->plan_id;
+  m.block_m = block_m_for(plan->cfg.head_dim);
 
   const int passes = (int)plan->item_pass.size() - 1;
   for (int p = 0; p < passes; ++p) {

@@ -18,20 +18,23 @@
 
 namespace dpp {
 
-// Packed query rows per tile. A packed row is (token, q head within the kv head's group);
-// row R of a request covers token R / group and q head kv_head * group + R % group.
-constexpr int kBlockM = 128;
-// Keys per KV tile. Tiles start at absolute key positions 0, 64, 128, ...
-constexpr int kBlockN = 64;
+// Tile geometry: constants of head_dim, never of the batch.
+// A packed query row is (token, q head within the kv head's group); row R of a request covers
+// token R / group and q head kv_head * group + R % group. Each wave owns 32 packed rows (two
+// 16-row MFMA column blocks); a workgroup is 8 waves (two per SIMD) at head_dim 128 and 4 waves
+// (one per SIMD, for the register file) at head_dim 256.
+constexpr int kRowsPerWave = 32;
+DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 128 ? 8 : 4; }
+DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) { return kRowsPerWave * waves_for(head_dim); }
+// Keys per KV tile. Tiles start at absolute key positions 0, BN, 2BN, ...
+DPP_HOST_DEVICE constexpr int block_n_for(int head_dim) { return head_dim <= 128 ? 64 : 32; }
+constexpr int kMaxBlockM = 256;
+constexpr int kMergeThreads = 256;
+
 // Fixed KV split length (the model-serving-minefield issue #73 correction comment,
 // "What the flag actually does", item 2). Splits start at absolute positions 0, 4096, ...
 constexpr int kSplitTokens = 4096;
-constexpr int kTilesPerSplit = kSplitTokens / kBlockN;
-static_assert(kSplitTokens % kBlockN == 0, "splits must be whole KV tiles");
-
-constexpr int kThreads = 256;  // four wave64 per workgroup, 32 packed rows each
-constexpr int kWaves = kThreads / 64;
-static_assert(kWaves * 32 == kBlockM, "each wave owns 32 packed rows");
+static_assert(kSplitTokens % 64 == 0 && kSplitTokens % 32 == 0, "splits must be whole KV tiles");
 
 constexpr uint32_t kHeaderMagic = 0x44505031u;  // "DPP1"
 constexpr int kHeaderWords = 16;                // fixed preamble (see HeaderPreamble)
@@ -50,10 +53,10 @@ struct RequestDesc {
 // One (q tile, KV split) unit of the prefill kernel, for every kv head (grid.y).
 struct PrefillItem {
   int32_t request;
-  int32_t row_start;     // first packed row of the tile (multiple of kBlockM)
+  int32_t row_start;     // first packed row of the tile (multiple of block_m_for(head_dim))
   int32_t split;         // split index s; keys [s*4096, (s+1)*4096)
   int32_t tile_splits;   // splits the tile's last row needs (S_t)
-  int32_t kv_tile_begin; // first KV tile (absolute, units of kBlockN)
+  int32_t kv_tile_begin; // first KV tile (absolute, units of block_n_for(head_dim))
   int32_t kv_tile_end;   // one past the last KV tile this item visits
   int32_t slot_base;     // first partial slot of the tile in this pass, -1 if S_t == 1
   int32_t pad;
@@ -68,9 +71,9 @@ struct MergeItem {
 };
 
 // Partial slot of (kv head c, split s, tile-local row lr) inside a tile's slot block.
-DPP_HOST_DEVICE inline int64_t partial_slot(int32_t slot_base, int32_t tile_splits, int c,
-                                                int s, int lr) {
-  return (int64_t)slot_base + ((int64_t)c * tile_splits + s) * kBlockM + lr;
+DPP_HOST_DEVICE inline int64_t partial_slot(int32_t slot_base, int32_t tile_splits, int c, int s,
+                                            int lr, int block_m) {
+  return (int64_t)slot_base + ((int64_t)c * tile_splits + s) * block_m + lr;
 }
 
 struct HeaderPreamble {
@@ -123,6 +126,7 @@ struct MergeArgs {
   int32_t num_merges;
   int32_t num_qo_heads;
   int32_t group;
+  int32_t block_m;
 };
 
 // Standalone merge over [rows, splits, heads, D] partials with natural-log lse.

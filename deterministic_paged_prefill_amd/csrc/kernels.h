@@ -7,8 +7,8 @@
 
 namespace dpp {
 
-// One prefill pass: grid (num_items, num_kv_heads), kThreads threads, dynamic LDS for the
-// tile buffers and the item's page-id table.
+// One prefill pass: grid (num_items, num_kv_heads), 64 * waves_for(head_dim) threads, dynamic
+// LDS for the tile buffers and the item's page-id table.
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, hipStream_t stream);
 
 // Merge of the split partials of one pass: grid (num_merges, num_kv_heads).

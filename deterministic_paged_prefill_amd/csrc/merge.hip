@@ -64,16 +64,16 @@ __device__ inline f32x4 merge4(int S, LseAt lse2_at, OAt o_at, float* lse2_out) 
 
 // Planned merge: grid (merges in pass, kv heads); each block merges one q tile's rows.
 template <int D>
-__global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int kTpr = D / 4;              // threads per row (4 columns each)
-  constexpr int kRowsPerPass = kThreads / kTpr;
+  constexpr int kRowsPerPass = kMergeThreads / kTpr;
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
   if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
   const MergeItem mi = reinterpret_cast<const MergeItem*>(a.header + pre->merge_offset)[a.merge_begin + blockIdx.x];
   const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[mi.request];
   const int kvh = blockIdx.y;
   const int g = a.group;
-  const int tile_rows = min(kBlockM, rq.qo_len * g - mi.row_start);
+  const int tile_rows = min(a.block_m, rq.qo_len * g - mi.row_start);
   const int ctx = rq.kv_len - rq.qo_len;
   const int col = (threadIdx.x % kTpr) * 4;
   for (int lr = threadIdx.x / kTpr; lr < tile_rows; lr += kRowsPerPass) {
@@ -83,10 +83,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
     const int S = p / kSplitTokens + 1;
     if (S < 2) continue;  // finished by the prefill kernel
     auto lse_at = [&](int s) {
-      return a.part_lse2[partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr)];
+      return a.part_lse2[partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr, a.block_m)];
     };
     auto o_at = [&](int s) {
-      return *reinterpret_cast<const f32x4*>(a.part_o + partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr) * D + col);
+      return *reinterpret_cast<const f32x4*>(a.part_o + partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr, a.block_m) * D + col);
     };
     float lse2;
     const f32x4 o = merge4(S, lse_at, o_at, &lse2);
@@ -98,10 +98,10 @@ __global__ __launch_bounds__(kThreads) void merge_kernel(MergeArgs a) {
 }
 
 // Standalone merge: one wave per (row, head); natural-log lse converted to base 2 on load.
-__global__ __launch_bounds__(kThreads) void merge_dense_kernel(MergeDenseArgs a) {
+__global__ __launch_bounds__(kMergeThreads) void merge_dense_kernel(MergeDenseArgs a) {
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int64_t rh = (int64_t)blockIdx.x * kWaves + wave;
+  const int64_t rh = (int64_t)blockIdx.x * (kMergeThreads / 64) + wave;
   if (rh >= a.num_rows * a.num_heads) return;
   const int64_t r = rh / a.num_heads;
   const int h = (int)(rh - r * a.num_heads);
@@ -126,9 +126,9 @@ __global__ __launch_bounds__(kThreads) void merge_dense_kernel(MergeDenseArgs a)
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream) {
   dim3 grid((unsigned)a.num_merges, (unsigned)num_kv_heads);
   if (head_dim == 128)
-    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 256)
-    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kThreads), 0, stream, a);
+    hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kMergeThreads), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -136,9 +136,10 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipS
 
 hipError_t launch_merge_dense(const MergeDenseArgs& a, hipStream_t stream) {
   const int64_t waves = a.num_rows * a.num_heads;
-  const int64_t blocks = (waves + kWaves - 1) / kWaves;
+  const int64_t per_block = kMergeThreads / 64;
+  const int64_t blocks = (waves + per_block - 1) / per_block;
   if (blocks > 0x7FFFFFFF) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(merge_dense_kernel, dim3((unsigned)blocks), dim3(kThreads), 0, stream, a);
+  hipLaunchKernelGGL(merge_dense_kernel, dim3((unsigned)blocks), dim3(kMergeThreads), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,12 +1,12 @@
 // Host planner: batch shape -> work list. Pure integer host code; no HIP calls.
 //
 // What it decides, and what it never decides:
-//  * tile geometry (kBlockM packed rows x kBlockN keys) and the 4096-token split length are
-//    constants; nothing here reads the batch's average or maximum query length (the sglang
+//  * tile geometry (block_m_for(head_dim) packed rows x block_n_for(head_dim) keys) and the
+//    4096-token split length are constants of the configuration; nothing here reads the batch's average or maximum query length (the sglang
 //    PR #46351 page, "Root cause", is the failure this avoids);
 //  * a request's query block is right-aligned to its KV: row i sits at position
 //    kv_len - qo_len + i (same page, "Fix" section);
-//  * a q tile visits KV tiles 0 .. floor(p_max / 64) of every split its last row reaches;
+//  * a q tile visits KV tiles 0 .. floor(p_max / BN) of every split its last row reaches;
 //    rows needing one split finish in the prefill kernel, longer rows leave one partial per
 //    split in the workspace and are combined by the merge kernel;
 //  * passes: partials are bounded by the caller's cap by running tiles in several launches
@@ -93,6 +93,9 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   const int32_t group = c.num_qo_heads / c.num_kv_heads;
   const int64_t P = c.page_size;
 
+  const int32_t block_n = block_n_for(c.head_dim);
+  const int32_t block_m = block_m_for(c.head_dim);
+  const int32_t tiles_per_split = kSplitTokens / block_n;
   std::vector<RequestDesc> reqs((size_t)batch_size);
   std::vector<TileInfo> tiles;
   for (int32_t r = 0; r < batch_size; ++r) {
@@ -114,13 +117,13 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
                                      std::to_string(qo_len) + " > kv_len " + std::to_string(kv_len));
     reqs[(size_t)r] = RequestDesc{qo_indptr[r], (int32_t)qo_len, kv_indptr[r], (int32_t)kv_len};
     const int64_t packed = qo_len * group;
-    if (packed > std::numeric_limits<int32_t>::max() - kBlockM)
+    if (packed > std::numeric_limits<int32_t>::max() - block_m)
       return fail(DPP_ERR_UNSUPPORTED, "too many query rows in request " + std::to_string(r));
-    for (int64_t rs = 0; rs < packed; rs += kBlockM) {
+    for (int64_t rs = 0; rs < packed; rs += block_m) {
       TileInfo t{};
       t.request = r;
       t.row_start = (int32_t)rs;
-      t.rows = (int32_t)std::min<int64_t>(kBlockM, packed - rs);
+      t.rows = (int32_t)std::min<int64_t>(block_m, packed - rs);
       t.p_max = kv_len - qo_len + (rs + t.rows - 1) / group;
       t.splits = (int32_t)(t.p_max / kSplitTokens + 1);
       tiles.push_back(t);
@@ -146,11 +149,11 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     slot_limit = std::min<int64_t>(slot_limit, max_slots_for(workspace_cap - header_bytes, c.head_dim));
   }
 
-  // Passes: tiles in request order; a tile needing partials takes S_t * Hkv * kBlockM slots.
+  // Passes: tiles in request order; a tile needing partials takes S_t * Hkv * block_m slots.
   int32_t pass = 0;
   int64_t used = 0, max_used = 0;
   for (auto& t : tiles) {
-    const int64_t need = t.splits > 1 ? (int64_t)t.splits * c.num_kv_heads * kBlockM : 0;
+    const int64_t need = t.splits > 1 ? (int64_t)t.splits * c.num_kv_heads * block_m : 0;
     if (need > slot_limit)
       return fail(DPP_ERR_WORKSPACE,
                   "workspace cap too small: one q tile needs " +
@@ -194,18 +197,18 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     while (tile_cursor < tiles.size() && tiles[tile_cursor].pass == p) {
       const TileInfo& t = tiles[tile_cursor++];
       const RequestDesc& rq = reqs[(size_t)t.request];
-      const int64_t last_tile = t.p_max / kBlockN;
+      const int64_t last_tile = t.p_max / block_n;
       for (int32_t s = 0; s < t.splits; ++s) {
         PrefillItem it{};
         it.request = t.request;
         it.row_start = t.row_start;
         it.split = s;
         it.tile_splits = t.splits;
-        it.kv_tile_begin = s * kTilesPerSplit;
-        it.kv_tile_end = (int32_t)std::min<int64_t>((int64_t)(s + 1) * kTilesPerSplit, last_tile + 1);
+        it.kv_tile_begin = s * tiles_per_split;
+        it.kv_tile_end = (int32_t)std::min<int64_t>((int64_t)(s + 1) * tiles_per_split, last_tile + 1);
         it.slot_base = (int32_t)t.slot_base;
-        const int64_t key_lo = (int64_t)it.kv_tile_begin * kBlockN;
-        const int64_t key_hi = std::min<int64_t>((int64_t)it.kv_tile_end * kBlockN, rq.kv_len);
+        const int64_t key_lo = (int64_t)it.kv_tile_begin * block_n;
+        const int64_t key_hi = std::min<int64_t>((int64_t)it.kv_tile_end * block_n, rq.kv_len);
         if (key_hi > key_lo) max_page_span = std::max(max_page_span, (key_hi - 1) / P - key_lo / P + 1);
         items.push_back(it);
       }
@@ -261,8 +264,8 @@ extern "C" size_t dpp_plan_workspace_bytes(const dpp_plan* plan) {
 
 extern "C" dpp_status dpp_plan_get_info(const dpp_plan* plan, dpp_plan_info* info) {
   if (!plan || !info) return fail(DPP_ERR_INVALID, "dpp_plan_get_info: null argument");
-  info->block_m = kBlockM;
-  info->block_n = kBlockN;
+  info->block_m = block_m_for(plan->cfg.head_dim);
+  info->block_n = block_n_for(plan->cfg.head_dim);
   info->split_tokens = kSplitTokens;
   info->num_passes = (int32_t)plan->item_pass.size() - 1;
   info->num_prefill_items = plan->num_items;

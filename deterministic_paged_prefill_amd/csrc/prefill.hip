@@ -1,31 +1,36 @@
 // Causal GQA prefill attention over a paged KV cache, gfx950 (CDNA4), wave64.
 //
-// One workgroup = one (q tile of kBlockM packed rows, KV split, kv head). Four waves each own
-// 32 packed rows. Per KV tile of kBlockN = 64 keys:
-//   gather   K and V rows through the page table into LDS (K row-major, V transposed),
-//            keys past kv_len zero-filled; fp8 E4M3 pages are decoded to bf16 on the way;
-//   QK^T     S^T[key, row] = K Q^T on v_mfma_f32_32x32x16_bf16, fp32 accumulation over
-//            head_dim in ascending 16-wide chunks (keys on M, this wave's 32 rows on N, so
-//            every lane holds scores of a single query row);
-//   mask     keys past the row's position p = kv_len - qo_len + token get -inf (a select
-//            after identical arithmetic; tiles wholly below the diagonal skip the select,
-//            which would not change a bit there);
+// One workgroup = one (q tile, KV split, kv head). Each wave owns 32 packed rows as two 16-row
+// MFMA column blocks; 8 waves (two per SIMD, 256-row tiles) at head_dim 128, 4 waves (one per
+// SIMD, 128-row tiles) at head_dim 256. Per KV tile of BN keys (64 at head_dim 128, 32 at
+// head_dim 256; tiles start at absolute multiples of BN):
+//   gather   every thread loads 16-byte chunks of K and V rows through the page table into
+//            registers, PF tiles ahead, then stores them into two LDS stages (natural
+//            [key][d] layout, 16-byte chunks XOR-swizzled by key). Keys past kv_len or on an
+//            out-of-range page are zero-filled; fp8 E4M3 chunks are decoded to bf16 on the way.
+//   QK^T     S^T[key, row] = K Q^T on v_mfma_f32_16x16x32_bf16, fp32 accumulation over
+//            head_dim in ascending 32-wide chunks: keys on M, 16 query rows on N, so a lane
+//            holds scores of a single query row (4 keys of every 16-key block).
+//   mask     keys past the row's position p = kv_len - qo_len + token get -inf (a select after
+//            identical arithmetic; tiles wholly below the diagonal skip the select, which
+//            would change no bit there).
 //   softmax  online, fp32, base 2: m' = max(m, max_j s_j); alpha = 1 if m' == m else
-//            exp2(m*c - m'*c); P_j = exp2(fma(s_j, c, -m'*c)); l = fma(l, alpha, sum_j P_j)
-//            with the row sum taken in one fixed tree (c = sm_scale * log2 e);
-//   PV       O^T[d, row] = alpha * O^T + V^T P^T on the same MFMA, P rounded to bf16 (RNE).
-// After a split's last tile a row either writes o = O / l (bf16) and lse = (m*c + log2 l) ln 2,
-// or -- when its keys reach past 4096 -- writes the split's fp32 partial (O / l, m*c + log2 l)
-// for the merge kernel.
+//            exp2(m c - m' c); P_j = exp2(fma(s_j, c, -m' c)); l = fma(l, alpha, sum_j P_j)
+//            (c = sm_scale log2 e). Row max and row sum: one fixed pairwise tree over the
+//            lane's values, then a butterfly over the four lanes holding the row.
+//   PV       O^T[d, row] = alpha O^T + V^T P^T on the same MFMA, P rounded to bf16 (RNE). The
+//            V^T operand comes straight from the natural layout through ds_read_tr16_b64.
+// After a split's last tile a row writes o = O / l (bf16) and lse = (m c + log2 l) ln 2, or, if
+// its keys reach past one 4096-token split, the split's fp32 partial (O / l, m c + log2 l).
 //
 // Why this is batch invariant: a row's bits depend on its query, keys 0..p, the tile and split
-// grid (absolute positions), the MFMA shapes and the code above. Which tile, wave or lane the
-// row lands in, how many rows share its tile, and how many other requests run beside it do
-// not enter its arithmetic: rows never mix inside an MFMA column, every lane runs the same
-// reduction tree, and tiles past a row's position are exact no-ops for it (alpha = 1, P = 0,
-// V zero-filled past kv_len). This replaces the fix the sglang PR #46351 page describes
-// (front-padding q so FlashInfer keeps its q-tile size) with a design that has no
-// batch-dependent choice to pin.
+// grid (absolute positions), the MFMA shapes and the code above -- not on which tile, wave or
+// lane holds it, how many rows share its tile, or what else is in the batch. Rows never mix in
+// an MFMA column, every lane runs the same reduction trees, and a tile past a row's position is
+// an exact no-op for it (alpha = 1, P = 0, V zero-filled past kv_len), so a block of rows may
+// skip such tiles. The sglang PR #46351 page ("Root cause") shows FlashInfer losing this by
+// sizing its q tile from the batch's average query length; here no launch choice enters the
+// arithmetic.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -38,30 +43,42 @@ namespace dpp {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+#define DPP_LDS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.693147180559945309417f;
 
 template <int D>
-struct Geometry {
-  static constexpr int kChunks = D / 8;                 // 16-byte bf16 chunks per K/V row
-  static constexpr int kRowsPerPass = kThreads / kChunks;
-  static constexpr int kPasses = kBlockN / kRowsPerPass;  // K rows each thread stages
-  static constexpr int kGroupsPerPass = kThreads / kChunks;  // 4-key groups per V pass
-  static constexpr int kVPasses = kBlockN / (4 * kGroupsPerPass);
-  static constexpr int kStrideK = D + 8;       // bf16 elements per K row in LDS (16 B pad)
-  static constexpr int kStrideV = kBlockN + 4;  // bf16 elements per V^T row in LDS (8 B pad)
-  static constexpr int kBytesK = kBlockN * kStrideK * 2;
-  static constexpr int kBytesV = D * kStrideV * 2;
-  static constexpr int kDChunks = D / 16;  // MFMA k-steps over head_dim
-  static constexpr int kDBlocks = D / 32;  // 32-row blocks of O^T
-  static_assert(kPasses * kRowsPerPass == kBlockN, "K staging");
-  static_assert(kVPasses * 4 * kGroupsPerPass == kBlockN, "V staging");
+struct Cfg {
+  static constexpr int THREADS = 64 * waves_for(D);
+  static constexpr int BM = block_m_for(D);        // packed query rows per tile
+  static constexpr int BN = block_n_for(D);        // keys per KV tile
+  static constexpr int CH = D / 8;                 // 16-byte bf16 chunks per K/V row
+  static constexpr int ROW_BYTES = D * 2;
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one of K or V, bf16
+  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
+  static constexpr int NS = 2;                     // LDS stages (one barrier per tile)
+  static constexpr int CPT = BN * CH / THREADS;    // chunks per thread per tensor per tile
+  static constexpr int KB = BN / 16;               // 16-key blocks (QK M blocks)
+  static constexpr int DC = D / 32;                // 32-wide head_dim chunks (QK k-steps)
+  static constexpr int DB = D / 16;                // 16-wide head_dim blocks (PV M blocks)
+  static constexpr int KC = BN / 32;               // 32-key chunks (PV k-steps)
+  static constexpr int NB = kRowsPerWave / 16;     // 16-row column blocks per wave
+  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
+  static_assert(CPT * THREADS == BN * CH, "staging covers the tile");
+  static_assert(CH >= 16, "swizzle needs 16 chunks per row");
+  static_assert(KC >= 1 && KB == 2 * KC, "tile shape");
 };
+
+// Byte offset of 16-byte chunk c of key row `key` inside a K or V tile.
+template <int ROW_BYTES>
+__device__ inline int chunk_off(int key, int c) {
+  return key * ROW_BYTES + ((c ^ (key & 15)) << 4);
+}
 
 // OCP E4M3 code -> fp32 (exact): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
 // S.1111.111 is NaN, no infinities.
@@ -69,9 +86,7 @@ __device__ inline float e4m3_to_f32(uint32_t code) {
   const uint32_t sign = (code & 0x80u) << 24;
   const uint32_t em = code & 0x7Fu;
   if (em == 0x7Fu) return __uint_as_float(0x7FC00000u | sign);
-  if (em < 8u) {  // subnormal: m * 2^-9
-    return __uint_as_float(sign | __float_as_uint((float)em * 0.001953125f));
-  }
+  if (em < 8u) return __uint_as_float(sign | __float_as_uint((float)em * 0.001953125f));
   return __uint_as_float(sign | ((em + (120u << 3)) << 20));
 }
 
@@ -81,92 +96,49 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// 8 E4M3 codes (two dwords) -> 8 bf16 (four dwords), value = decode(code) * scale.
+// 8 E4M3 codes -> 8 bf16, value = decode(code) * scale (exact for power-of-two scales).
 __device__ inline u32x4 dequant8(u32x2 raw, float scale) {
   u32x4 out;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
     const uint32_t x = raw[w];
-    const float f0 = e4m3_to_f32(x & 0xFFu) * scale;
-    const float f1 = e4m3_to_f32((x >> 8) & 0xFFu) * scale;
-    const float f2 = e4m3_to_f32((x >> 16) & 0xFFu) * scale;
-    const float f3 = e4m3_to_f32(x >> 24) * scale;
-    out[2 * w] = pack_bf16x2(f0, f1);
-    out[2 * w + 1] = pack_bf16x2(f2, f3);
+    out[2 * w] = pack_bf16x2(e4m3_to_f32(x & 0xFFu) * scale, e4m3_to_f32((x >> 8) & 0xFFu) * scale);
+    out[2 * w + 1] = pack_bf16x2(e4m3_to_f32((x >> 16) & 0xFFu) * scale, e4m3_to_f32(x >> 24) * scale);
   }
   return out;
 }
 
-// Raw storage of one staged 8-element chunk: 16 B (bf16) or 8 B (fp8).
 template <bool FP8>
-struct Chunk;
+struct Raw;
 template <>
-struct Chunk<false> {
+struct Raw<false> {
   u32x4 v;
 };
 template <>
-struct Chunk<true> {
+struct Raw<true> {
   u32x2 v;
 };
 
-template <int D, bool FP8>
-__device__ inline Chunk<FP8> load_chunk(const void* pool, int64_t elem) {
-  Chunk<FP8> c;
-  if constexpr (FP8) {
-    c.v = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(pool) + elem);
-  } else {
-    c.v = *reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(pool) + elem);
-  }
-  return c;
+__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <bool FP8>
-__device__ inline Chunk<FP8> zero_chunk() {
-  Chunk<FP8> c;
-  if constexpr (FP8) {
-    c.v = u32x2{0u, 0u};
-  } else {
-    c.v = u32x4{0u, 0u, 0u, 0u};
-  }
-  return c;
+// Butterfly over the four lanes (l, l^16, l^32, l^48) holding one query row. Each step
+// combines a value with its partner's, so every lane of the row ends with the same bits.
+__device__ inline float row_max4(float x) {
+  x = fmaxf(x, __shfl_xor(x, 16));
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+__device__ inline float row_sum4(float x) {
+  x = x + __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 
-template <bool FP8>
-__device__ inline u32x4 to_bf16(const Chunk<FP8>& c, float scale) {
-  if constexpr (FP8) {
-    return dequant8(c.v, scale);
-  } else {
-    (void)scale;
-    return c.v;
-  }
-}
-
-// Element offset of (token j, kv head c, chunk ch) in a pool, or -1 when j is past kv_len or
-// its page id is out of range (the chunk is then staged as zeros).
-__device__ inline int64_t pool_offset(int j, int kv_len, int key_lo_page, int page_size,
-                                      int page_shift, const int32_t* pg_lds, int64_t num_pages,
-                                      int64_t token_stride, int64_t head_off) {
-  if (j >= kv_len) return -1;
-  int pi, slot;
-  if (page_shift >= 0) {
-    pi = j >> page_shift;
-    slot = j & (page_size - 1);
-  } else {
-    pi = j / page_size;
-    slot = j - pi * page_size;
-  }
-  const int64_t page = pg_lds[pi - key_lo_page];
-  if (page < 0 || page >= num_pages) return -1;
-  return (page * page_size + slot) * token_stride + head_off;
-}
-
-template <int D, bool FP8>
-__global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
-  using G = Geometry<D>;
+template <int D, bool FP8, int PF>
+__global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
+  using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint16_t* k_lds = reinterpret_cast<uint16_t*>(smem);
-  uint16_t* vt_lds = reinterpret_cast<uint16_t*>(smem + G::kBytesK);
-  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + G::kBytesK + G::kBytesV);
+  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + C::LDS_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -180,256 +152,301 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillArgs a) {
   const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[it.request];
 
   const int g = a.group;
-  const int rows_total = rq.qo_len * g;
-  const int tile_rows = min(kBlockM, rows_total - it.row_start);
+  const int tile_rows = min(C::BM, rq.qo_len * g - it.row_start);
   const int ctx = rq.kv_len - rq.qo_len;  // position of query token 0
-  const int n = lane & 31;                  // this lane's query row within the wave
-  const int hf = lane >> 5;                 // which half of the MFMA k-group the lane feeds
-  const int lr = wave * 32 + n;             // tile-local packed row
-  const int R = it.row_start + lr;
-  const bool row_valid = lr < tile_rows;
-  const int token = R / g;
-  const int qhead = kvh * g + (R - token * g);
-  // Rows past the tile are given a position no key reaches, so they stay finite (q = 0).
-  const int p = row_valid ? ctx + token : INT_MAX;
-  const int p_min = ctx + it.row_start / g;  // smallest position in the tile
+  const int lg = lane >> 4;                // 16-lane group: 8-wide k slice in, 4 output rows out
+  const int li = lane & 15;                // column (query row) within a 16-row block
   const int split_key0 = it.split * kSplitTokens;
+
+  // Rows of this lane: tile-local packed row lr = 32*wave + 16*nb + li.
+  int p_row[C::NB];    // position of the row (INT_MAX past the tile: no key is masked)
+  int nb_pmax[C::NB];  // wave-uniform: largest position among the block's valid rows, -1 if none
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int lr0 = wave * kRowsPerWave + nb * 16;
+    const int lr = lr0 + li;
+    p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
+    nb_pmax[nb] = lr0 < tile_rows ? ctx + (it.row_start + min(lr0 + 15, tile_rows - 1)) / g : -1;
+  }
+  const int p_min = ctx + it.row_start / g;
 
   // ---- page ids of the keys this item visits -> LDS
   const int page_size = a.page_size;
   const int page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz(page_size) : -1;
-  const int key_lo = it.kv_tile_begin * kBlockN;
-  const int key_hi = min(it.kv_tile_end * kBlockN, rq.kv_len);
+  const int key_lo = it.kv_tile_begin * C::BN;
+  const int key_hi = min(it.kv_tile_end * C::BN, rq.kv_len);
   const int key_lo_page = key_lo / page_size;
   const int n_pages = key_hi > key_lo ? (key_hi - 1) / page_size - key_lo_page + 1 : 0;
-  for (int i = tid; i < n_pages; i += kThreads) pg_lds[i] = a.kv_indices[rq.page_start + key_lo_page + i];
+  for (int i = tid; i < n_pages; i += C::THREADS) pg_lds[i] = a.kv_indices[rq.page_start + key_lo_page + i];
 
-  // ---- this lane's query row, as the MFMA B operand (16-byte chunks of head_dim)
-  bf16x8 qreg[G::kDChunks];
-  {
-    const uint16_t* qrow = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((int64_t)(rq.q_start + token) * a.num_qo_heads + qhead) * D + hf * 8;
+  // ---- query rows as the QK^T B operand: lane (lg, li) holds head_dim [32dc + 8lg, +8)
+  bf16x8 qreg[C::NB][C::DC];
 #pragma unroll
-    for (int kc = 0; kc < G::kDChunks; ++kc) {
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int lr = wave * kRowsPerWave + nb * 16 + li;
+    const bool valid = lr < tile_rows;
+    const int R = it.row_start + lr;
+    const int token = R / g;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                         ((int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g)) * D + 8 * lg;
+#pragma unroll
+    for (int dc = 0; dc < C::DC; ++dc) {
       u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (row_valid) v = *reinterpret_cast<const u32x4*>(qrow + kc * 16);
-      qreg[kc] = __builtin_bit_cast(bf16x8, v);
+      if (valid) v = *reinterpret_cast<const u32x4*>(qp + dc * 32);
+      qreg[nb][dc] = __builtin_bit_cast(bf16x8, v);
     }
   }
   __syncthreads();  // page table visible
 
-  // ---- staging assignments
+  // ---- staging: this thread moves chunks q = tid + THREADS*i (key q / CH, chunk q % CH)
   const int64_t token_stride = (int64_t)a.num_kv_heads * D;
   const int64_t head_off = (int64_t)kvh * D;
-  const int kch = tid % G::kChunks;     // chunk this thread stages
-  const int krow0 = tid / G::kChunks;   // first K row
-  const int vgrp0 = tid / G::kChunks;   // first 4-key V group
-  Chunk<FP8> kst[G::kPasses];
-  Chunk<FP8> vst[G::kVPasses][4];
+  Raw<FP8> kst[PF][C::CPT], vst[PF][C::CPT];
 
-  auto load_tile = [&](int kt) {
-    const int base = kt * kBlockN;
+  auto load_tile = [&](int slot, int kt) {
 #pragma unroll
-    for (int i = 0; i < G::kPasses; ++i) {
-      const int j = base + krow0 + i * G::kRowsPerPass;
-      const int64_t off = pool_offset(j, rq.kv_len, key_lo_page, page_size, page_shift, pg_lds,
-                                      a.num_pages, token_stride, head_off);
-      kst[i] = off >= 0 ? load_chunk<D, FP8>(a.k_pool, off + kch * 8) : zero_chunk<FP8>();
-    }
-#pragma unroll
-    for (int i = 0; i < G::kVPasses; ++i) {
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int j = base + 4 * (vgrp0 + i * G::kGroupsPerPass) + e;
-        const int64_t off = pool_offset(j, rq.kv_len, key_lo_page, page_size, page_shift, pg_lds,
-                                        a.num_pages, token_stride, head_off);
-        vst[i][e] = off >= 0 ? load_chunk<D, FP8>(a.v_pool, off + kch * 8) : zero_chunk<FP8>();
+    for (int i = 0; i < C::CPT; ++i) {
+      const int q = tid + C::THREADS * i;
+      const int j = kt * C::BN + q / C::CH;
+      const int ch = q % C::CH;
+      int64_t off = -1;
+      if (j < rq.kv_len) {
+        int pi, sl;
+        if (page_shift >= 0) {
+          pi = j >> page_shift;
+          sl = j & (page_size - 1);
+        } else {
+          pi = j / page_size;
+          sl = j - pi * page_size;
+        }
+        const int64_t page = pg_lds[pi - key_lo_page];
+        if (page >= 0 && page < a.num_pages) off = (page * page_size + sl) * token_stride + head_off + ch * 8;
+      }
+      if constexpr (FP8) {
+        const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_pool);
+        const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_pool);
+        kst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x2*>(kp + off) : u32x2{0u, 0u};
+        vst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x2*>(vp + off) : u32x2{0u, 0u};
+      } else {
+        const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pool);
+        const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pool);
+        kst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x4*>(kp + off) : u32x4{0u, 0u, 0u, 0u};
+        vst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x4*>(vp + off) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   };
 
-  auto store_tile = [&]() {
+  auto store_tile = [&](int slot, int stage) {
+    unsigned char* kt_lds = smem + stage * C::STAGE_BYTES;
+    unsigned char* vt_lds = kt_lds + C::TILE_BYTES;
 #pragma unroll
-    for (int i = 0; i < G::kPasses; ++i) {
-      const int r = krow0 + i * G::kRowsPerPass;
-      *reinterpret_cast<u32x4*>(k_lds + r * G::kStrideK + kch * 8) = to_bf16<FP8>(kst[i], a.k_scale);
-    }
-#pragma unroll
-    for (int i = 0; i < G::kVPasses; ++i) {
-      const int k0 = 4 * (vgrp0 + i * G::kGroupsPerPass);
-      u32x4 rows[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) rows[e] = to_bf16<FP8>(vst[i][e], a.v_scale);
-      // transpose: element t of the chunk, keys k0..k0+3 -> V^T[kch*8 + t][k0 .. k0+3]
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int w = t >> 1;
-        const int sh = (t & 1) * 16;
-        const uint32_t x0 = (rows[0][w] >> sh) & 0xFFFFu;
-        const uint32_t x1 = (rows[1][w] >> sh) & 0xFFFFu;
-        const uint32_t x2 = (rows[2][w] >> sh) & 0xFFFFu;
-        const uint32_t x3 = (rows[3][w] >> sh) & 0xFFFFu;
-        *reinterpret_cast<u32x2*>(vt_lds + (kch * 8 + t) * G::kStrideV + k0) =
-            u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+    for (int i = 0; i < C::CPT; ++i) {
+      const int q = tid + C::THREADS * i;
+      const int off = chunk_off<C::ROW_BYTES>(q / C::CH, q % C::CH);
+      if constexpr (FP8) {
+        *reinterpret_cast<u32x4*>(kt_lds + off) = dequant8(kst[slot][i].v, a.k_scale);
+        *reinterpret_cast<u32x4*>(vt_lds + off) = dequant8(vst[slot][i].v, a.v_scale);
+      } else {
+        *reinterpret_cast<u32x4*>(kt_lds + off) = kst[slot][i].v;
+        *reinterpret_cast<u32x4*>(vt_lds + off) = vst[slot][i].v;
       }
     }
   };
 
-  // ---- online-softmax state of this lane's row
+  // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
-  float m_raw = -INFINITY;  // running max of raw scores
-  float m_sc = -INFINITY;   // m_raw * c
-  float l = 0.f;
-  f32x16 acc[G::kDBlocks];
+  float m_raw[C::NB], m_sc[C::NB], l_sum[C::NB];
+  f32x4 acc[C::DB][C::NB];
 #pragma unroll
-  for (int db = 0; db < G::kDBlocks; ++db)
+  for (int nb = 0; nb < C::NB; ++nb) {
+    m_raw[nb] = -INFINITY;
+    m_sc[nb] = -INFINITY;
+    l_sum[nb] = 0.f;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[db][r] = 0.f;
+    for (int db = 0; db < C::DB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
-  load_tile(it.kv_tile_begin);
-  for (int kt = it.kv_tile_begin; kt < it.kv_tile_end; ++kt) {
-    __syncthreads();  // everyone is done reading the previous tile
-    store_tile();
-    __syncthreads();  // tile kt visible
-    if (kt + 1 < it.kv_tile_end) load_tile(kt + 1);
+  const int kt0 = it.kv_tile_begin;
+  const int kt1 = it.kv_tile_end;
+  // Tile T lives in register slot (T - kt0) % PF until it is stored into LDS stage
+  // (T - kt0) % NS. Prologue: tiles kt0 .. kt0+PF-1 in flight, tile kt0 stored, its slot
+  // refilled with tile kt0+PF.
+#pragma unroll
+  for (int s = 0; s < PF; ++s)
+    if (kt0 + s < kt1) load_tile(s, kt0 + s);
+  store_tile(0, 0);
+  if (kt0 + PF < kt1) load_tile(0, kt0 + PF);
+  __syncthreads();
 
-    // S^T = K Q^T for keys [kt*64, kt*64+64): two 32-key blocks
-    f32x16 s[2];
+  // Per tile: store tile kt+1 into its stage (that stage was last read two tiles ago, before
+  // the previous barrier), refill the freed slot with tile kt+1+PF, compute tile kt, barrier.
+  // Unrolled by PF so every register slot index is a compile-time constant.
+  for (int base = kt0; base < kt1; base += PF) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 accs;
+    for (int u = 0; u < PF; ++u) {
+      const int kt = base + u;
+      if (kt >= kt1) break;
+      const int rel = kt - kt0;
+      if (kt + 1 < kt1) store_tile((u + 1) % PF, (rel + 1) % C::NS);
+      if (kt + 1 + PF < kt1) load_tile((u + 1) % PF, kt + 1 + PF);
+
+      const unsigned char* k_lds = smem + (rel % C::NS) * C::STAGE_BYTES;
+      const unsigned char* v_lds = k_lds + C::TILE_BYTES;
+      const int key0 = kt * C::BN;
+      const bool diag = key0 + C::BN - 1 > p_min;
+
+      // A 16-row block has work in this tile when one of its valid rows reaches key0.
+      bool act[C::NB];
+      bool any = false;
 #pragma unroll
-      for (int r = 0; r < 16; ++r) accs[r] = 0.f;
-      const uint16_t* krow = k_lds + (kb * 32 + n) * G::kStrideK + hf * 8;
-#pragma unroll
-      for (int kc = 0; kc < G::kDChunks; ++kc) {
-        const bf16x8 kv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(krow + kc * 16));
-        accs = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kv, qreg[kc], accs, 0, 0, 0);
+      for (int nb = 0; nb < C::NB; ++nb) {
+        act[nb] = nb_pmax[nb] >= key0;
+        any = any || act[nb];
       }
-      s[kb] = accs;
-    }
-
-    // causal mask: key index of s[kb][r] is kt*64 + kb*32 + (r/4)*8 + hf*4 + r%4
-    const int key0 = kt * kBlockN;
-    if (key0 + kBlockN - 1 > p_min) {
+      if (any) {
+        // S^T = K Q^T
+        f32x4 s[C::KB][C::NB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < C::KB; ++kb) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + kb * 32 + (r >> 2) * 8 + hf * 4 + (r & 3);
-          s[kb][r] = key > p ? -INFINITY : s[kb][r];
+          for (int nb = 0; nb < C::NB; ++nb) s[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int dc = 0; dc < C::DC; ++dc) {
+            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + chunk_off<C::ROW_BYTES>(kb * 16 + li, dc * 4 + lg));
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+              if (act[nb]) s[kb][nb] = mfma16(ka, qreg[nb][dc], s[kb][nb]);
+          }
         }
-    }
-
-    // row max: this lane's 32 scores, then the partner lane holding the row's other 32
-    float mx = s[0][0];
+        // causal mask: s[kb][nb][j] holds key key0 + 16kb + 4lg + j of row p_row[nb]
+        if (diag) {
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+          for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-
-    const float m_new = fmaxf(m_raw, mx);
-    const float m_new_sc = m_new * c;
-    const float alpha = (m_new == m_raw) ? 1.f : __builtin_amdgcn_exp2f(m_sc - m_new_sc);
-    m_raw = m_new;
-    m_sc = m_new_sc;
-
-    float pv[2][16];
+            for (int nb = 0; nb < C::NB; ++nb)
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+              for (int j = 0; j < 4; ++j) {
+                const int key = key0 + kb * 16 + lg * 4 + j;
+                s[kb][nb][j] = key > p_row[nb] ? -INFINITY : s[kb][nb][j];
+              }
+        }
+        // online softmax, per 16-row block
+        bf16x8 pb[C::KC][C::NB];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) pv[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c, -m_new_sc));
-
-    // row sum: fixed pairwise tree over the lane's 32 values, then + partner's
-    float t16[16];
+        for (int nb = 0; nb < C::NB; ++nb) {
+          if (!act[nb]) continue;
+          float mx = s[0][nb][0];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) t16[i] = pv[i >> 3][(2 * i) & 15] + pv[i >> 3][(2 * i + 1) & 15];
+          for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-    for (int w = 8; w >= 1; w >>= 1)
+            for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kb][nb][j]);
+          mx = row_max4(mx);
+          const float m_new = fmaxf(m_raw[nb], mx);
+          const float m_new_sc = m_new * c;
+          const float alpha = (m_new == m_raw[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_sc[nb] - m_new_sc);
+          m_raw[nb] = m_new;
+          m_sc[nb] = m_new_sc;
+          float pv[C::KB][4];
 #pragma unroll
-      for (int i = 0; i < w; ++i) t16[i] = t16[2 * i] + t16[2 * i + 1];
-    const float rs = t16[0] + __shfl_xor(t16[0], 32);
-    l = __builtin_fmaf(l, alpha, rs);
-
-    if (__any(alpha != 1.f)) {  // acc * 1 == acc: skipping keeps every bit
+          for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-      for (int db = 0; db < G::kDBlocks; ++db)
+            for (int j = 0; j < 4; ++j) pv[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][nb][j], c, -m_new_sc));
+          // row sum: pairs within each 4-key group, then a pairwise tree over the groups
+          float t[C::KB];
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[db][r] *= alpha;
-    }
-
-    // O^T += V^T P^T. MFMA (kb, u) covers keys kb*32 + 16u + [0, 16); its k index
-    // 8*hf + t is key kb*32 + 16u + 8*(t/4) + 4*hf + t%4, i.e. the lane's P values
-    // s[kb][8u .. 8u+7] and V^T rows read at those key offsets.
+          for (int kb = 0; kb < C::KB; ++kb) t[kb] = (pv[kb][0] + pv[kb][1]) + (pv[kb][2] + pv[kb][3]);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+          for (int w = C::KB / 2; w >= 1; w >>= 1)
 #pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        u32x4 pb;
+            for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
+          const float rs = row_sum4(t[0]);
+          l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha, rs);
+          if (__any(alpha != 1.f)) {  // acc * 1 == acc: skipping keeps every bit
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pb[w] = pack_bf16x2(pv[kb][8 * u + 2 * w], pv[kb][8 * u + 2 * w + 1]);
-        const bf16x8 pbf = __builtin_bit_cast(bf16x8, pb);
-        const int kofs = kb * 32 + 16 * u + 4 * hf;
+            for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha;
+          }
+          // P^T as the PV B operand: k = 8lg + t is key 32kc + 16(t/4) + 4lg + t%4
 #pragma unroll
-        for (int db = 0; db < G::kDBlocks; ++db) {
-          const uint16_t* vrow = vt_lds + (db * 32 + n) * G::kStrideV + kofs;
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const bf16x8 va = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pbf, acc[db], 0, 0, 0);
+          for (int kc = 0; kc < C::KC; ++kc) {
+            const u32x4 w4 = u32x4{pack_bf16x2(pv[2 * kc][0], pv[2 * kc][1]),
+                                   pack_bf16x2(pv[2 * kc][2], pv[2 * kc][3]),
+                                   pack_bf16x2(pv[2 * kc + 1][0], pv[2 * kc + 1][1]),
+                                   pack_bf16x2(pv[2 * kc + 1][2], pv[2 * kc + 1][3])};
+            pb[kc][nb] = __builtin_bit_cast(bf16x8, w4);
+          }
+        }
+        // O^T += V^T P^T. V^T comes transposed from the natural layout: lane (lg, r) of read h
+        // points at key 32kc + 16h + 4lg + r/4, head_dim 16db + 4(r%4), and receives
+        // V[32kc + 16h + 4lg + j][16db + li] for j = 0..3 -- the A operand's k = 8lg + 4h + j.
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+          for (int kc = 0; kc < C::KC; ++kc) {
+            s16x4 hv[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
+              const int e = db * 16 + 4 * (li & 3);
+              const unsigned char* addr = v_lds + chunk_off<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
+              hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
+            }
+            const s16x8 v8 = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
+            const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+            for (int nb = 0; nb < C::NB; ++nb)
+              if (act[nb]) acc[db][nb] = mfma16(va, pb[kc][nb], acc[db][nb]);
+          }
         }
       }
+      __syncthreads();
     }
   }
 
-  // ---- epilogue: this lane holds O^T[d][row] for d = db*32 + (r/4)*8 + 4*hf + r%4
-  if (!row_valid || p < split_key0) return;  // not a row of this split
-  const float inv_l = 1.f / l;
-  const float lse2 = m_sc + __builtin_amdgcn_logf(l);
-  const int row_splits = p / kSplitTokens + 1;
-  if (row_splits == 1) {
-    const int64_t orow = (int64_t)(rq.q_start + token) * a.num_qo_heads + qhead;
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + orow * D + 4 * hf;
+  // ---- epilogue: lane holds O^T[d = 16db + 4lg + j][row 16nb + li]
 #pragma unroll
-    for (int db = 0; db < G::kDBlocks; ++db)
+  for (int nb = 0; nb < C::NB; ++nb) {
+    const int lr = wave * kRowsPerWave + nb * 16 + li;
+    const int p = p_row[nb];
+    if (lr >= tile_rows || p < split_key0) continue;  // not a row of this split
+    const int R = it.row_start + lr;
+    const int token = R / g;
+    const float inv_l = 1.f / l_sum[nb];
+    const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l_sum[nb]);
+    if (p / kSplitTokens == 0) {
+      const int64_t orow = (int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g);
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + orow * D + 4 * lg;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i;
-        *reinterpret_cast<u32x2*>(op + db * 32 + i * 8) =
-            u32x2{pack_bf16x2(acc[db][r] * inv_l, acc[db][r + 1] * inv_l),
-                  pack_bf16x2(acc[db][r + 2] * inv_l, acc[db][r + 3] * inv_l)};
-      }
-    if (hf == 0) a.lse[orow] = lse2 * kLn2;
-  } else {
-    const int64_t slot = partial_slot(it.slot_base, it.tile_splits, kvh, it.split, lr);
-    float* pp = a.part_o + slot * D + 4 * hf;
+      for (int db = 0; db < C::DB; ++db)
+        *reinterpret_cast<u32x2*>(op + db * 16) =
+            u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
+                  pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
+      if (lg == 0) a.lse[orow] = lse2 * kLn2;
+    } else {
+      const int64_t slot = partial_slot(it.slot_base, it.tile_splits, kvh, it.split, lr, C::BM);
+      float* pp = a.part_o + slot * D + 4 * lg;
 #pragma unroll
-    for (int db = 0; db < G::kDBlocks; ++db)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 4 * i;
-        *reinterpret_cast<f32x4*>(pp + db * 32 + i * 8) =
-            f32x4{acc[db][r] * inv_l, acc[db][r + 1] * inv_l, acc[db][r + 2] * inv_l, acc[db][r + 3] * inv_l};
-      }
-    if (hf == 0) a.part_lse2[slot] = lse2;
+      for (int db = 0; db < C::DB; ++db)
+        *reinterpret_cast<f32x4*>(pp + db * 16) =
+            f32x4{acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l, acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l};
+      if (lg == 0) a.part_lse2[slot] = lse2;
+    }
   }
 }
 
-template <int D, bool FP8>
+template <int D, bool FP8, int PF>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  using G = Geometry<D>;
-  const size_t lds = (size_t)G::kBytesK + G::kBytesV + (size_t)a.page_slots * 4;
+  using C = Cfg<D>;
+  const size_t lds = (size_t)C::LDS_BYTES + (size_t)a.page_slots * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, PF>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
   }
   dim3 grid((unsigned)a.num_items, (unsigned)a.num_kv_heads);
-  hipLaunchKernelGGL((prefill_kernel<D, FP8>), grid, dim3(kThreads), lds, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, PF>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -437,8 +454,8 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
 
 hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {
   const bool fp8 = kv_dtype == 1;
-  if (head_dim == 128) return fp8 ? launch_one<128, true>(a, stream) : launch_one<128, false>(a, stream);
-  if (head_dim == 256) return fp8 ? launch_one<256, true>(a, stream) : launch_one<256, false>(a, stream);
+  if (head_dim == 128) return fp8 ? launch_one<128, true, 2>(a, stream) : launch_one<128, false, 2>(a, stream);
+  if (head_dim == 256) return fp8 ? launch_one<256, true, 2>(a, stream) : launch_one<256, false, 2>(a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -69,13 +69,13 @@ def _specs_batch(specs, page=16, g=4):
     return b
 
 
-def _coverage(parsed, g, hkv=8):
-    """Map (request, packed row, split) -> set of KV tiles visited; check exactly-once."""
+def _coverage(parsed, g, bm):
+    """Map (request, packed row, split) -> KV tile range visited; check exactly-once."""
     seen = {}
     for it in parsed.items:
         r, rs, s, S, kb, ke, slot, _ = (int(x) for x in it)
         q_start, qo_len, page_start, kv_len = parsed.requests[r]
-        rows = min(128, qo_len * g - rs)
+        rows = min(bm, qo_len * g - rs)
         for lr in range(rows):
             key = (r, rs + lr, s)
             assert key not in seen, f"row {key} covered twice"
@@ -91,8 +91,11 @@ def test_every_key_covered_once_per_split(dpp, specs):
     g = 4
     b = _specs_batch(specs)
     p = _plan(dpp, b)
+    bm, bn = p.info.block_m, p.info.block_n
+    assert (bm, bn) == dpp.tile_shape(128)
+    tps = 4096 // bn
     parsed = parse(p.header())
-    cov = _coverage(parsed, g)
+    cov = _coverage(parsed, g, bm)
     expected = set()
     for r, (kv, qlen) in enumerate(specs):
         for R in range(qlen * g):
@@ -102,9 +105,9 @@ def test_every_key_covered_once_per_split(dpp, specs):
                 expected.add((r, R, s))
                 kb, ke = cov[(r, R, s)]
                 # the item visits every tile holding keys s*4096 .. min(p, split end)
-                assert kb == s * 64
-                assert ke * 64 > min(pos, (s + 1) * 4096 - 1)
-                assert ke <= (s + 1) * 64
+                assert kb == s * tps
+                assert ke * bn > min(pos, (s + 1) * 4096 - 1)
+                assert ke <= (s + 1) * tps
     # rows may ride along in items of splits they do not need (tile-mates' splits); the
     # kernel skips their writes. Every needed (row, split) is present:
     assert expected <= set(cov)
@@ -126,17 +129,18 @@ def test_workspace_closed_form_single_pass(dpp):
     specs = [(9000, 9000), (5000, 40), (100, 100)]
     b = _specs_batch(specs)
     p = _plan(dpp, b)
+    bm = p.info.block_m
     parsed = parse(p.header())
     slots = 0
     ntile = 0
     for kv, qlen in specs:
-        for rs in range(0, qlen * 4, 128):
-            rows = min(128, qlen * 4 - rs)
+        for rs in range(0, qlen * 4, bm):
+            rows = min(bm, qlen * 4 - rs)
             pmax = kv - qlen + (rs + rows - 1) // 4
             S = pmax // 4096 + 1
             ntile += 1
             if S > 1:
-                slots += S * 8 * 128
+                slots += S * 8 * bm
     words = 16 + 4 * len(specs) + 8 * len(parsed.items) + 4 * len(parsed.merges)
     hdr = _align(words * 4)
     assert p.info.header_bytes == hdr
