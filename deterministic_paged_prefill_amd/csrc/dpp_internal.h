@@ -85,9 +85,10 @@ struct HeaderPreamble {
   int32_t item_offset;
   int32_t merge_offset;
   uint32_t plan_id;        // unique per plan; kernels refuse a header with another id
-  int32_t reserved[kHeaderWords - 8];
+  int32_t reserved[kHeaderWords - 8];  // zero; the gather reads its first 16 bytes as a zero chunk
 };
 static_assert(sizeof(HeaderPreamble) == kHeaderWords * 4, "preamble size");
+static_assert(offsetof(HeaderPreamble, reserved) % 16 == 0, "zero chunk must be 16-byte aligned");
 
 // ---- kernel launch arguments ----
 

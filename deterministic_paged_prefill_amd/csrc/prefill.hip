@@ -138,11 +138,11 @@ template <int D, bool FP8, int PF>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
   using C = Cfg<D>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + C::LDS_BYTES);
+  int64_t* pg_lds = reinterpret_cast<int64_t*>(smem + C::LDS_BYTES);  // page byte offsets, -1 = bad id
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
   const int kvh = blockIdx.y;
 
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
@@ -169,6 +169,9 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     nb_pmax[nb] = lr0 < tile_rows ? ctx + (it.row_start + min(lr0 + 15, tile_rows - 1)) / g : -1;
   }
   const int p_min = ctx + it.row_start / g;
+  int wave_pmax = -1;  // largest position among the wave's valid rows
+#pragma unroll
+  for (int nb = 0; nb < C::NB; ++nb) wave_pmax = max(wave_pmax, nb_pmax[nb]);
 
   // ---- page ids of the keys this item visits -> LDS
   const int page_size = a.page_size;
@@ -177,7 +180,13 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int key_hi = min(it.kv_tile_end * C::BN, rq.kv_len);
   const int key_lo_page = key_lo / page_size;
   const int n_pages = key_hi > key_lo ? (key_hi - 1) / page_size - key_lo_page + 1 : 0;
-  for (int i = tid; i < n_pages; i += C::THREADS) pg_lds[i] = a.kv_indices[rq.page_start + key_lo_page + i];
+  constexpr int kElemBytes = FP8 ? 1 : 2;
+  const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElemBytes;
+  const int64_t page_bytes = token_bytes * page_size;
+  for (int i = tid; i < n_pages; i += C::THREADS) {
+    const int64_t id = a.kv_indices[rq.page_start + key_lo_page + i];
+    pg_lds[i] = (id >= 0 && id < a.num_pages) ? id * page_bytes : -1;
+  }
 
   // ---- query rows as the QK^T B operand: lane (lg, li) holds head_dim [32dc + 8lg, +8)
   bf16x8 qreg[C::NB][C::DC];
@@ -199,39 +208,52 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   __syncthreads();  // page table visible
 
   // ---- staging: this thread moves chunks q = tid + THREADS*i (key q / CH, chunk q % CH)
-  const int64_t token_stride = (int64_t)a.num_kv_heads * D;
-  const int64_t head_off = (int64_t)kvh * D;
   Raw<FP8> kst[PF][C::CPT], vst[PF][C::CPT];
 
+  // Branch-free gather (a branch around each load would keep the compiler from counting
+  // outstanding loads, and it would then wait for every prefetched tile at each LDS store):
+  // a chunk past kv_len, or on a page id outside the pool, reads 16 zero bytes from the
+  // preamble's reserved words instead. When the page size is a power of two no larger than
+  // a KV tile, a thread's page slot and in-page offset are the same for every tile.
+  const unsigned char* zero16 = reinterpret_cast<const unsigned char*>(pre->reserved);
+  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k_pool);
+  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v_pool);
+  const bool pow2_pages = page_shift >= 0 && page_size <= C::BN;
+  int kr[C::CPT];          // key row of the tile this thread stages
+  int pg_rel[C::CPT];      // its page, relative to the tile's first page (pow2_pages)
+  int64_t in_page[C::CPT]; // byte offset inside the page: slot, kv head, chunk
+#pragma unroll
+  for (int i = 0; i < C::CPT; ++i) {
+    const int q = tid + C::THREADS * i;
+    kr[i] = q / C::CH;
+    const int64_t chunk_bytes = ((int64_t)kvh * D + (q % C::CH) * 8) * kElemBytes;
+    pg_rel[i] = pow2_pages ? (kr[i] >> page_shift) : 0;
+    in_page[i] = (pow2_pages ? (int64_t)(kr[i] & (page_size - 1)) * token_bytes : 0) + chunk_bytes;
+  }
   auto load_tile = [&](int slot, int kt) {
+    const int tile_page = pow2_pages ? ((kt * C::BN) >> page_shift) - key_lo_page : 0;
 #pragma unroll
     for (int i = 0; i < C::CPT; ++i) {
-      const int q = tid + C::THREADS * i;
-      const int j = kt * C::BN + q / C::CH;
-      const int ch = q % C::CH;
-      int64_t off = -1;
-      if (j < rq.kv_len) {
-        int pi, sl;
-        if (page_shift >= 0) {
-          pi = j >> page_shift;
-          sl = j & (page_size - 1);
-        } else {
-          pi = j / page_size;
-          sl = j - pi * page_size;
-        }
-        const int64_t page = pg_lds[pi - key_lo_page];
-        if (page >= 0 && page < a.num_pages) off = (page * page_size + sl) * token_stride + head_off + ch * 8;
-      }
-      if constexpr (FP8) {
-        const uint8_t* kp = reinterpret_cast<const uint8_t*>(a.k_pool);
-        const uint8_t* vp = reinterpret_cast<const uint8_t*>(a.v_pool);
-        kst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x2*>(kp + off) : u32x2{0u, 0u};
-        vst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x2*>(vp + off) : u32x2{0u, 0u};
+      const int j = kt * C::BN + kr[i];
+      int64_t off;
+      if (pow2_pages) {
+        off = pg_lds[tile_page + pg_rel[i]];
+        off = off < 0 ? off : off + in_page[i];
       } else {
-        const uint16_t* kp = reinterpret_cast<const uint16_t*>(a.k_pool);
-        const uint16_t* vp = reinterpret_cast<const uint16_t*>(a.v_pool);
-        kst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x4*>(kp + off) : u32x4{0u, 0u, 0u, 0u};
-        vst[slot][i].v = off >= 0 ? *reinterpret_cast<const u32x4*>(vp + off) : u32x4{0u, 0u, 0u, 0u};
+        const int jj = min(j, rq.kv_len - 1);
+        const int pi = jj / page_size;
+        const int64_t po = pg_lds[pi - key_lo_page];
+        off = po < 0 ? po : po + (int64_t)(jj - pi * page_size) * token_bytes + in_page[i];
+      }
+      const bool ok = j < rq.kv_len && off >= 0;
+      const unsigned char* kp = ok ? kbase + off : zero16;
+      const unsigned char* vp = ok ? vbase + off : zero16;
+      if constexpr (FP8) {
+        kst[slot][i].v = *reinterpret_cast<const u32x2*>(kp);
+        vst[slot][i].v = *reinterpret_cast<const u32x2*>(vp);
+      } else {
+        kst[slot][i].v = *reinterpret_cast<const u32x4*>(kp);
+        vst[slot][i].v = *reinterpret_cast<const u32x4*>(vp);
       }
     }
   };
@@ -270,12 +292,14 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int kt1 = it.kv_tile_end;
   // Tile T lives in register slot (T - kt0) % PF until it is stored into LDS stage
   // (T - kt0) % NS. Prologue: tiles kt0 .. kt0+PF-1 in flight, tile kt0 stored, its slot
-  // refilled with tile kt0+PF.
+  // refilled with tile kt0+PF. Loads are issued unconditionally (tile numbers past the end
+  // re-read the last tile, which is never stored): with every load on every path the
+  // compiler can wait for exactly one tile at each store instead of for all of them.
+  const int kt_last = kt1 - 1;
 #pragma unroll
-  for (int s = 0; s < PF; ++s)
-    if (kt0 + s < kt1) load_tile(s, kt0 + s);
+  for (int s = 0; s < PF; ++s) load_tile(s, min(kt0 + s, kt_last));
   store_tile(0, 0);
-  if (kt0 + PF < kt1) load_tile(0, kt0 + PF);
+  load_tile(0, min(kt0 + PF, kt_last));
   __syncthreads();
 
   // Per tile: store tile kt+1 into its stage (that stage was last read two tiles ago, before
@@ -285,25 +309,20 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 #pragma unroll
     for (int u = 0; u < PF; ++u) {
       const int kt = base + u;
-      if (kt >= kt1) break;
+      const bool live = kt < kt1;  // the last unrolled group may run past the item's tiles
       const int rel = kt - kt0;
       if (kt + 1 < kt1) store_tile((u + 1) % PF, (rel + 1) % C::NS);
-      if (kt + 1 + PF < kt1) load_tile((u + 1) % PF, kt + 1 + PF);
+      load_tile((u + 1) % PF, min(kt + 1 + PF, kt_last));
 
       const unsigned char* k_lds = smem + (rel % C::NS) * C::STAGE_BYTES;
       const unsigned char* v_lds = k_lds + C::TILE_BYTES;
       const int key0 = kt * C::BN;
       const bool diag = key0 + C::BN - 1 > p_min;
 
-      // A 16-row block has work in this tile when one of its valid rows reaches key0.
-      bool act[C::NB];
-      bool any = false;
-#pragma unroll
-      for (int nb = 0; nb < C::NB; ++nb) {
-        act[nb] = nb_pmax[nb] >= key0;
-        any = any || act[nb];
-      }
-      if (any) {
+      // The wave has work in this tile when one of its valid rows reaches key0. Its blocks
+      // then all run the same straight-line code: for a row that does not reach key0 every
+      // score is masked, alpha = 1 and P = 0, so the tile changes none of its state.
+      if (live && wave_pmax >= key0) {
         // S^T = K Q^T
         f32x4 s[C::KB][C::NB];
 #pragma unroll
@@ -315,7 +334,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
             const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + chunk_off<C::ROW_BYTES>(kb * 16 + li, dc * 4 + lg));
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb)
-              if (act[nb]) s[kb][nb] = mfma16(ka, qreg[nb][dc], s[kb][nb]);
+              s[kb][nb] = mfma16(ka, qreg[nb][dc], s[kb][nb]);
           }
         }
         // causal mask: s[kb][nb][j] holds key key0 + 16kb + 4lg + j of row p_row[nb]
@@ -334,7 +353,6 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         bf16x8 pb[C::KC][C::NB];
 #pragma unroll
         for (int nb = 0; nb < C::NB; ++nb) {
-          if (!act[nb]) continue;
           float mx = s[0][nb][0];
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
@@ -394,7 +412,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
             const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
 #pragma unroll
             for (int nb = 0; nb < C::NB; ++nb)
-              if (act[nb]) acc[db][nb] = mfma16(va, pb[kc][nb], acc[db][nb]);
+              acc[db][nb] = mfma16(va, pb[kc][nb], acc[db][nb]);
           }
         }
       }
@@ -436,7 +454,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 template <int D, bool FP8, int PF>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   using C = Cfg<D>;
-  const size_t lds = (size_t)C::LDS_BYTES + (size_t)a.page_slots * 4;
+  const size_t lds = (size_t)C::LDS_BYTES + (size_t)a.page_slots * 8;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
