@@ -21,11 +21,14 @@ namespace dpp {
 // Tile geometry: constants of head_dim, never of the batch.
 // A packed query row is (token, q head within the kv head's group); row R of a request covers
 // token R / group and q head kv_head * group + R % group. Each wave owns 32 packed rows (two
-// 16-row MFMA column blocks); a workgroup is 8 waves (two per SIMD) at head_dim 128 and 4 waves
-// (one per SIMD, for the register file) at head_dim 256.
-constexpr int kRowsPerWave = 32;
+// 16-row MFMA column blocks); a workgroup is 8 waves (two per SIMD, so one wave's softmax
+// overlaps the other's MFMAs) at head_dim 128 and 4 waves (one per SIMD, for the register
+// file) at head_dim 256.
+DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim > 0 ? 32 : 32; }
 DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 128 ? 8 : 4; }
-DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) { return kRowsPerWave * waves_for(head_dim); }
+DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) {
+  return rows_per_wave_for(head_dim) * waves_for(head_dim);
+}
 // Keys per KV tile. Tiles start at absolute key positions 0, BN, 2BN, ...
 DPP_HOST_DEVICE constexpr int block_n_for(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 constexpr int kMaxBlockM = 256;

@@ -14,21 +14,22 @@
 //   mask     keys past the row's position p = kv_len - qo_len + token get -inf (a select after
 //            identical arithmetic; tiles wholly below the diagonal skip the select, which
 //            would change no bit there).
-//   softmax  online, fp32, base 2: m' = max(m, max_j s_j); alpha = 1 if m' == m else
-//            exp2(m c - m' c); P_j = exp2(fma(s_j, c, -m' c)); l = fma(l, alpha, sum_j P_j)
-//            (c = sm_scale log2 e). Row max and row sum: one fixed pairwise tree over the
-//            lane's values, then a butterfly over the four lanes holding the row.
+//   softmax  online, fp32, base 2, with a lazily moved reference max r (c = sm_scale log2 e):
+//            t = c max_j s_j; if t > r + 8 then r' = t, alpha = exp2(r - r') else r' = r,
+//            alpha = 1; P_j = exp2(fma(s_j, c, -r')) (so P_j <= 2^8); l = fma(l, alpha, sum_j P_j);
+//            O = alpha O. Row max and row sum: one fixed pairwise tree over the lane's values,
+//            then a butterfly over the four lanes holding the row.
 //   PV       O^T[d, row] = alpha O^T + V^T P^T on the same MFMA, P rounded to bf16 (RNE). The
 //            V^T operand comes straight from the natural layout through ds_read_tr16_b64.
-// After a split's last tile a row writes o = O / l (bf16) and lse = (m c + log2 l) ln 2, or, if
-// its keys reach past one 4096-token split, the split's fp32 partial (O / l, m c + log2 l).
+// After a split's last tile a row writes o = O / l (bf16) and lse = (r + log2 l) ln 2, or, if
+// its keys reach past one 4096-token split, the split's fp32 partial (O / l, r + log2 l).
 //
 // Why this is batch invariant: a row's bits depend on its query, keys 0..p, the tile and split
 // grid (absolute positions), the MFMA shapes and the code above -- not on which tile, wave or
 // lane holds it, how many rows share its tile, or what else is in the batch. Rows never mix in
-// an MFMA column, every lane runs the same reduction trees, and a tile past a row's position is
-// an exact no-op for it (alpha = 1, P = 0, V zero-filled past kv_len), so a block of rows may
-// skip such tiles. The sglang PR #46351 page ("Root cause") shows FlashInfer losing this by
+// an MFMA column, every lane runs the same reduction trees, the reference max follows the row's
+// own scores, and a tile past a row's position is an exact no-op for it (alpha = 1, P = 0, V
+// zero-filled past kv_len), so a wave may skip such tiles. The sglang PR #46351 page ("Root cause") shows FlashInfer losing this by
 // sizing its q tile from the batch's average query length; here no launch choice enters the
 // arithmetic.
 #include <hip/hip_runtime.h>
@@ -46,11 +47,15 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef short s16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define DPP_LDS __attribute__((address_space(3)))
 
 constexpr float kLn2 = 0.693147180559945309417f;
+// Rebase threshold of the online softmax's reference max, in log2 units (P_j <= 2^8).
+constexpr float kRebase = 8.0f;
 
 template <int D>
 struct Cfg {
@@ -67,17 +72,25 @@ struct Cfg {
   static constexpr int DC = D / 32;                // 32-wide head_dim chunks (QK k-steps)
   static constexpr int DB = D / 16;                // 16-wide head_dim blocks (PV M blocks)
   static constexpr int KC = BN / 32;               // 32-key chunks (PV k-steps)
-  static constexpr int NB = kRowsPerWave / 16;     // 16-row column blocks per wave
+  static constexpr int RPW = rows_per_wave_for(D);  // packed rows per wave
+  static constexpr int NB = RPW / 16;              // 16-row column blocks per wave
   static constexpr int LDS_BYTES = NS * STAGE_BYTES;
   static_assert(CPT * THREADS == BN * CH, "staging covers the tile");
   static_assert(CH >= 16, "swizzle needs 16 chunks per row");
   static_assert(KC >= 1 && KB == 2 * KC, "tile shape");
 };
 
-// Byte offset of 16-byte chunk c of key row `key` inside a K or V tile.
+// Byte offset of 16-byte chunk c of key row `key` inside the K tile. The XOR with key % 16
+// spreads the 16 key rows one QK^T operand read touches (same chunk) over all banks.
 template <int ROW_BYTES>
 __device__ inline int chunk_off(int key, int c) {
   return key * ROW_BYTES + ((c ^ (key & 15)) << 4);
+}
+// Same for the V tile, swizzled in 32-byte units: a transposing read takes 32 bytes from each
+// of 4 consecutive keys per 16 lanes (8 keys per 32 lanes), which this spreads over all banks.
+template <int ROW_BYTES>
+__device__ inline int chunk_off_v(int key, int c) {
+  return key * ROW_BYTES + ((c ^ ((key & 7) << 1)) << 4);
 }
 
 // OCP E4M3 code -> fp32 (exact): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
@@ -90,10 +103,9 @@ __device__ inline float e4m3_to_f32(uint32_t code) {
   return __uint_as_float(sign | ((em + (120u << 3)) << 20));
 }
 
+// Two fp32 -> two bf16, round to nearest even, in one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
-  const __bf16 a = (__bf16)lo;
-  const __bf16 b = (__bf16)hi;
-  return (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
 // 8 E4M3 codes -> 8 bf16, value = decode(code) * scale (exact for power-of-two scales).
@@ -123,15 +135,22 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Butterfly over the four lanes (l, l^16, l^32, l^48) holding one query row. Each step
-// combines a value with its partner's, so every lane of the row ends with the same bits.
+// Butterfly over the four lanes (l, l^16, l^32, l^48) holding one query row, on the gfx950
+// lane-swap instructions: permlane16_swap(x, x) hands every lane the pair {x[l & ~16],
+// x[l | 16]} and permlane32_swap(x, x) the pair {x[l & 31], x[(l & 31) + 32]}, always in that
+// order, so each lane of a row combines the same operands in the same order and ends with the
+// same bits: ((x0 + x1) + (x2 + x3)) for the sum.
 __device__ inline float row_max4(float x) {
-  x = fmaxf(x, __shfl_xor(x, 16));
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float row_sum4(float x) {
-  x = x + __shfl_xor(x, 16);
-  return x + __shfl_xor(x, 32);
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 template <int D, bool FP8, int PF>
@@ -163,7 +182,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   int nb_pmax[C::NB];  // wave-uniform: largest position among the block's valid rows, -1 if none
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    const int lr0 = wave * kRowsPerWave + nb * 16;
+    const int lr0 = wave * C::RPW + nb * 16;
     const int lr = lr0 + li;
     p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
     nb_pmax[nb] = lr0 < tile_rows ? ctx + (it.row_start + min(lr0 + 15, tile_rows - 1)) / g : -1;
@@ -192,7 +211,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   bf16x8 qreg[C::NB][C::DC];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    const int lr = wave * kRowsPerWave + nb * 16 + li;
+    const int lr = wave * C::RPW + nb * 16 + li;
     const bool valid = lr < tile_rows;
     const int R = it.row_start + lr;
     const int token = R / g;
@@ -265,23 +284,23 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     for (int i = 0; i < C::CPT; ++i) {
       const int q = tid + C::THREADS * i;
       const int off = chunk_off<C::ROW_BYTES>(q / C::CH, q % C::CH);
+      const int off_v = chunk_off_v<C::ROW_BYTES>(q / C::CH, q % C::CH);
       if constexpr (FP8) {
         *reinterpret_cast<u32x4*>(kt_lds + off) = dequant8(kst[slot][i].v, a.k_scale);
-        *reinterpret_cast<u32x4*>(vt_lds + off) = dequant8(vst[slot][i].v, a.v_scale);
+        *reinterpret_cast<u32x4*>(vt_lds + off_v) = dequant8(vst[slot][i].v, a.v_scale);
       } else {
         *reinterpret_cast<u32x4*>(kt_lds + off) = kst[slot][i].v;
-        *reinterpret_cast<u32x4*>(vt_lds + off) = vst[slot][i].v;
+        *reinterpret_cast<u32x4*>(vt_lds + off_v) = vst[slot][i].v;
       }
     }
   };
 
   // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
-  float m_raw[C::NB], m_sc[C::NB], l_sum[C::NB];
+  float m_sc[C::NB], l_sum[C::NB];  // reference max (scaled, base 2) and running sum per row
   f32x4 acc[C::DB][C::NB];
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    m_raw[nb] = -INFINITY;
     m_sc[nb] = -INFINITY;
     l_sum[nb] = 0.f;
 #pragma unroll
@@ -340,14 +359,13 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         // causal mask: s[kb][nb][j] holds key key0 + 16kb + 4lg + j of row p_row[nb]
         if (diag) {
 #pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb)
+          for (int nb = 0; nb < C::NB; ++nb) {
+            const int thr = p_row[nb] - key0 - 4 * lg;  // masked iff 16kb + j > thr
 #pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
+            for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-              for (int j = 0; j < 4; ++j) {
-                const int key = key0 + kb * 16 + lg * 4 + j;
-                s[kb][nb][j] = key > p_row[nb] ? -INFINITY : s[kb][nb][j];
-              }
+              for (int j = 0; j < 4; ++j) s[kb][nb][j] = (kb * 16 + j > thr) ? -INFINITY : s[kb][nb][j];
+          }
         }
         // online softmax, per 16-row block
         bf16x8 pb[C::KC][C::NB];
@@ -359,16 +377,19 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 #pragma unroll
             for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kb][nb][j]);
           mx = row_max4(mx);
-          const float m_new = fmaxf(m_raw[nb], mx);
-          const float m_new_sc = m_new * c;
-          const float alpha = (m_new == m_raw[nb]) ? 1.f : __builtin_amdgcn_exp2f(m_sc[nb] - m_new_sc);
-          m_raw[nb] = m_new;
-          m_sc[nb] = m_new_sc;
+          // The reference max moves only when this tile's max exceeds it by more than
+          // kRebase (and on the row's first keys); otherwise P_j <= 2^kRebase and O, l keep
+          // their scale. Same softmax, and O is rescaled only on the rare rebase.
+          const float mx_sc = mx * c;
+          const bool rebase = mx_sc > m_sc[nb] + kRebase;
+          const float m_use = rebase ? mx_sc : m_sc[nb];
+          const float alpha = rebase ? __builtin_amdgcn_exp2f(m_sc[nb] - m_use) : 1.f;
+          m_sc[nb] = m_use;
           float pv[C::KB][4];
 #pragma unroll
           for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) pv[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][nb][j], c, -m_new_sc));
+            for (int j = 0; j < 4; ++j) pv[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][nb][j], c, -m_use));
           // row sum: pairs within each 4-key group, then a pairwise tree over the groups
           float t[C::KB];
 #pragma unroll
@@ -379,7 +400,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
             for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
           const float rs = row_sum4(t[0]);
           l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha, rs);
-          if (__any(alpha != 1.f)) {  // acc * 1 == acc: skipping keeps every bit
+          if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha;
           }
@@ -405,7 +426,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
             for (int h = 0; h < 2; ++h) {
               const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
               const int e = db * 16 + 4 * (li & 3);
-              const unsigned char* addr = v_lds + chunk_off<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
+              const unsigned char* addr = v_lds + chunk_off_v<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
               hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
             }
             const s16x8 v8 = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
@@ -423,7 +444,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   // ---- epilogue: lane holds O^T[d = 16db + 4lg + j][row 16nb + li]
 #pragma unroll
   for (int nb = 0; nb < C::NB; ++nb) {
-    const int lr = wave * kRowsPerWave + nb * 16 + li;
+    const int lr = wave * C::RPW + nb * 16 + li;
     const int p = p_row[nb];
     if (lr >= tile_rows || p < split_key0) continue;  // not a row of this split
     const int R = it.row_start + lr;
