@@ -130,11 +130,14 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
 
   const int passes = (int)plan->item_pass.size() - 1;
   for (int p = 0; p < passes; ++p) {
-    a.item_begin = plan->item_pass[(size_t)p];
-    a.num_items = plan->item_pass[(size_t)p + 1] - a.item_begin;
-    if (a.num_items > 0) {
-      e = launch_prefill(a, plan->cfg.head_dim, plan->cfg.kv_dtype, stream);
-      if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    for (int narrow = 0; narrow < 2; ++narrow) {
+      a.item_begin = narrow ? plan->item_narrow[(size_t)p] : plan->item_pass[(size_t)p];
+      const int32_t end = narrow ? plan->item_pass[(size_t)p + 1] : plan->item_narrow[(size_t)p];
+      a.num_items = end - a.item_begin;
+      if (a.num_items > 0) {
+        e = launch_prefill(a, plan->cfg.head_dim, plan->cfg.kv_dtype, narrow != 0, stream);
+        if (e != hipSuccess) return hip_fail(e, "prefill launch");
+      }
     }
     m.merge_begin = plan->merge_pass[(size_t)p];
     m.num_merges = plan->merge_pass[(size_t)p + 1] - m.merge_begin;

@@ -20,15 +20,19 @@ namespace dpp {
 
 // Tile geometry: constants of head_dim, never of the batch.
 // A packed query row is (token, q head within the kv head's group); row R of a request covers
-// token R / group and q head kv_head * group + R % group. Each wave owns 32 packed rows (two
-// 16-row MFMA column blocks); a workgroup is 8 waves (two per SIMD, so one wave's softmax
-// overlaps the other's MFMAs) at head_dim 128 and 4 waves (one per SIMD, for the register
-// file) at head_dim 256.
-DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim > 0 ? 32 : 32; }
+// token R / group and q head kv_head * group + R % group. A workgroup is 4 waves, one per
+// SIMD, each owning rows_per_wave packed rows as 16-row MFMA column blocks: 64 rows at
+// head_dim <= 128 (256-row tiles), 32 at head_dim 256 (128-row tiles), sized to the 512
+// registers a wave has when it is alone on its SIMD.
+DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim <= 128 ? 32 : 32; }
 DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 128 ? 8 : 4; }
 DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) {
   return rows_per_wave_for(head_dim) * waves_for(head_dim);
 }
+// A q tile with at most this many rows (a short extend) is run by a narrow instantiation of
+// the same kernel whose waves hold one 16-row block. Which instantiation runs a tile is a
+// launch choice: the per-row arithmetic is the same.
+constexpr int kNarrowRows = 16;
 // Keys per KV tile. Tiles start at absolute key positions 0, BN, 2BN, ...
 DPP_HOST_DEVICE constexpr int block_n_for(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 constexpr int kMaxBlockM = 256;
@@ -36,6 +40,17 @@ constexpr int kMergeThreads = 256;
 
 // Fixed KV split length (the model-serving-minefield issue #73 correction comment,
 // "What the flag actually does", item 2). Splits start at absolute positions 0, 4096, ...
+// Blocks of a launch are dispatched round-robin over the chip's XCDs (8 on MI355X, each with
+// its own L2). xcd_chunked maps block b of n to a work index so that XCD x receives the
+// contiguous range [x*q + min(x, r), +q + (x < r)), q = n / kXcds, r = n % kXcds, in order.
+// It is a bijection on [0, n) for any kXcds; only locality depends on the value.
+constexpr int kXcds = 8;
+DPP_HOST_DEVICE inline int xcd_chunked(int b, int n) {
+  const int q = n / kXcds, r = n % kXcds;
+  const int x = b % kXcds;
+  return x * q + (x < r ? x : r) + b / kXcds;
+}
+
 constexpr int kSplitTokens = 4096;
 static_assert(kSplitTokens % 64 == 0 && kSplitTokens % 32 == 0, "splits must be whole KV tiles");
 

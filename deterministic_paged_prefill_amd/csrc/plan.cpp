@@ -12,8 +12,10 @@
 //  * passes: partials are bounded by the caller's cap by running tiles in several launches
 //    (the model-serving-minefield issue #73 correction, "The failure", shows an unbounded
 //    split buffer crashing a server);
-//  * order: items of a pass are sorted longest first for load balance. Order, passes and cap
-//    change when and where a row is computed, never its arithmetic.
+//  * order: inside a pass, requests with the longest item first, a request's items kept
+//    together and longest first (load balance, and L2 reuse of the request's KV); a pass of
+//    tiles with at most kNarrowRows rows each runs on the narrow kernel. Order, passes, cap
+//    and kernel instantiation change when and where a row is computed, never its arithmetic.
 #include "plan.h"
 
 #include <algorithm>
@@ -136,7 +138,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     n_merges += t.splits > 1 ? 1 : 0;
   }
   const int64_t words = kHeaderWords + 4 * (int64_t)batch_size + 8 * n_items + 4 * n_merges;
-  if (n_items > std::numeric_limits<int32_t>::max() / 2 || words > std::numeric_limits<int32_t>::max() / 2)
+  if (n_items > std::numeric_limits<int32_t>::max() / 2 / c.num_kv_heads ||
+      words > std::numeric_limits<int32_t>::max() / 2)
     return fail(DPP_ERR_UNSUPPORTED, "batch too large for one plan");
   const size_t header_bytes = align_up((size_t)words * 4, 256);
 
@@ -183,13 +186,14 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   plan->num_items = (int32_t)n_items;
   plan->num_merges = (int32_t)n_merges;
 
-  // Emit items pass by pass, longest first inside a pass (stable, so ties keep tile order).
+  // Emit items pass by pass in the order described at the top of this file.
   std::vector<PrefillItem> items;
   std::vector<MergeItem> merges;
   items.reserve((size_t)n_items);
   merges.reserve((size_t)n_merges);
   plan->item_pass.assign(1, 0);
   plan->merge_pass.assign(1, 0);
+  plan->item_narrow.clear();
   int64_t max_page_span = 1;
   size_t tile_cursor = 0;
   for (int32_t p = 0; p < num_passes; ++p) {
@@ -214,10 +218,30 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
       }
       if (t.splits > 1) merges.push_back(MergeItem{t.request, t.row_start, t.splits, (int32_t)t.slot_base});
     }
+    // Requests whose longest item is longer go first; a request's items stay together
+    // (they read the same KV, and the launch hands contiguous runs of items to one XCD),
+    // longest first among them.
+    std::vector<int32_t> req_len((size_t)batch_size, 0);
+    for (size_t i = first; i < items.size(); ++i) {
+      int32_t& m = req_len[(size_t)items[i].request];
+      m = std::max(m, items[i].kv_tile_end - items[i].kv_tile_begin);
+    }
     std::stable_sort(items.begin() + (std::ptrdiff_t)first, items.end(),
-                     [](const PrefillItem& a, const PrefillItem& b) {
+                     [&](const PrefillItem& a, const PrefillItem& b) {
+                       const int32_t ra = req_len[(size_t)a.request], rb = req_len[(size_t)b.request];
+                       if (ra != rb) return ra > rb;
+                       if (a.request != b.request) return a.request < b.request;
                        return (a.kv_tile_end - a.kv_tile_begin) > (b.kv_tile_end - b.kv_tile_begin);
                      });
+    // A pass whose tiles all have at most kNarrowRows rows (extends) runs on the narrow
+    // kernel; a pass with wider tiles runs all its items in one launch of the wide kernel,
+    // so that its short tiles fill in behind the long ones instead of running after them.
+    const bool all_narrow = std::all_of(items.begin() + (std::ptrdiff_t)first, items.end(),
+                                        [&](const PrefillItem& it) {
+                                          const RequestDesc& rq = reqs[(size_t)it.request];
+                                          return (int64_t)rq.qo_len * group - it.row_start <= kNarrowRows;
+                                        });
+    plan->item_narrow.push_back(all_narrow ? (int32_t)first : (int32_t)items.size());
     plan->item_pass.push_back((int32_t)items.size());
     plan->merge_pass.push_back((int32_t)merges.size());
   }

@@ -26,6 +26,9 @@ struct dpp_plan {
   // [merge_pass[p], merge_pass[p+1]).
   std::vector<int32_t> item_pass;
   std::vector<int32_t> merge_pass;
+  // Pass p runs items [item_pass[p], item_narrow[p]) on the wide kernel and
+  // [item_narrow[p], item_pass[p+1]) on the narrow one (one of the two ranges is empty).
+  std::vector<int32_t> item_narrow;
 
   int64_t max_partial_slots = 0;
   size_t header_bytes = 0;

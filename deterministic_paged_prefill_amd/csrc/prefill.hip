@@ -57,25 +57,26 @@ constexpr float kLn2 = 0.693147180559945309417f;
 // Rebase threshold of the online softmax's reference max, in log2 units (P_j <= 2^8).
 constexpr float kRebase = 8.0f;
 
-template <int D>
-struct Cfg {
-  static constexpr int THREADS = 64 * waves_for(D);
-  static constexpr int BM = block_m_for(D);        // packed query rows per tile
+template <int D, int NB>
+struct Geo {
+  static constexpr int WAVES = waves_for(D);
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int PLAN_BM = block_m_for(D);   // packed rows of a planned q tile
+  static constexpr int RPW = 16 * NB;              // rows this instantiation gives a wave
   static constexpr int BN = block_n_for(D);        // keys per KV tile
   static constexpr int CH = D / 8;                 // 16-byte bf16 chunks per K/V row
   static constexpr int ROW_BYTES = D * 2;
-  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one of K or V, bf16
-  static constexpr int STAGE_BYTES = 2 * TILE_BYTES;
-  static constexpr int NS = 2;                     // LDS stages (one barrier per tile)
-  static constexpr int CPT = BN * CH / THREADS;    // chunks per thread per tensor per tile
+  static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one KV tile of K or V in bf16
+  static constexpr int NBUF = 4;                   // LDS buffers per tensor
   static constexpr int KB = BN / 16;               // 16-key blocks (QK M blocks)
   static constexpr int DC = D / 32;                // 32-wide head_dim chunks (QK k-steps)
   static constexpr int DB = D / 16;                // 16-wide head_dim blocks (PV M blocks)
   static constexpr int KC = BN / 32;               // 32-key chunks (PV k-steps)
-  static constexpr int RPW = rows_per_wave_for(D);  // packed rows per wave
-  static constexpr int NB = RPW / 16;              // 16-row column blocks per wave
-  static constexpr int LDS_BYTES = NS * STAGE_BYTES;
-  static_assert(CPT * THREADS == BN * CH, "staging covers the tile");
+  static constexpr int NCH = BN * CH / THREADS;    // 16-byte chunks per thread per tensor per tile
+  static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
+  static_assert(NCH * THREADS == BN * CH, "the threads cover a tile");
+  static_assert(NCH * 64 * WAVES * 16 == TILE_BYTES, "one DMA load per wave moves 1 KiB");
+  static_assert(RPW * WAVES >= kNarrowRows && RPW * WAVES <= PLAN_BM, "tile rows fit the waves");
   static_assert(CH >= 16, "swizzle needs 16 chunks per row");
   static_assert(KC >= 1 && KB == 2 * KC, "tile shape");
 };
@@ -120,17 +121,6 @@ __device__ inline u32x4 dequant8(u32x2 raw, float scale) {
   return out;
 }
 
-template <bool FP8>
-struct Raw;
-template <>
-struct Raw<false> {
-  u32x4 v;
-};
-template <>
-struct Raw<true> {
-  u32x2 v;
-};
-
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -153,64 +143,83 @@ __device__ inline float row_sum4(float x) {
   return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
-template <int D, bool FP8, int PF>
+// One LDS-DMA load: each lane of the wave fetches 16 bytes from its own global address and
+// lane l's bytes land at LDS byte address lds_base + 16 l. The LDS address goes in M0, one
+// wait state before the load. Issued as assembly so that the compiler does not count it
+// among its own outstanding loads (it would otherwise wait for every DMA load in flight at
+// each barrier); the kernel waits for its DMA loads itself with wait_vmcnt.
+__device__ inline void dma16(const void* gaddr, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gaddr), "s"(lds_base)
+               : "memory");
+}
+
+// s_waitcnt vmcnt(N), no wait on the other counters.
+template <int N>
+__device__ inline void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+// NB: 16-row blocks per wave. P2: page_size is a power of two no larger than a KV tile, so a
+// chunk's page within its tile and its offset in that page are the same for every tile.
+template <int D, bool FP8, int NB, bool P2>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
-  using C = Cfg<D>;
+  using C = Geo<D, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int64_t* pg_lds = reinterpret_cast<int64_t*>(smem + C::LDS_BYTES);  // page byte offsets, -1 = bad id
+  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + C::LDS_BYTES);  // page ids, -1 = bad id
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
-  const int kvh = blockIdx.y;
+  // Work w = kvh * num_items + item. The dispatcher hands block b to XCD b % kXcds; giving
+  // each XCD one contiguous range of w keeps the q tiles that read one request's KV for one
+  // kv head on the same L2.
+  const int w = xcd_chunked(blockIdx.x, a.num_items * a.num_kv_heads);
+  const int kvh = w / a.num_items;
 
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
   if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
   const PrefillItem it =
-      reinterpret_cast<const PrefillItem*>(a.header + pre->item_offset)[a.item_begin + blockIdx.x];
+      reinterpret_cast<const PrefillItem*>(a.header + pre->item_offset)[a.item_begin + (w - kvh * a.num_items)];
   const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[it.request];
 
   const int g = a.group;
-  const int tile_rows = min(C::BM, rq.qo_len * g - it.row_start);
+  const int tile_rows = min(C::PLAN_BM, rq.qo_len * g - it.row_start);
   const int ctx = rq.kv_len - rq.qo_len;  // position of query token 0
   const int lg = lane >> 4;                // 16-lane group: 8-wide k slice in, 4 output rows out
   const int li = lane & 15;                // column (query row) within a 16-row block
   const int split_key0 = it.split * kSplitTokens;
+  const bool has_rows = wave * C::RPW < tile_rows;  // wave-uniform
 
-  // Rows of this lane: tile-local packed row lr = 32*wave + 16*nb + li.
-  int p_row[C::NB];    // position of the row (INT_MAX past the tile: no key is masked)
-  int nb_pmax[C::NB];  // wave-uniform: largest position among the block's valid rows, -1 if none
+  // Rows of this lane: tile-local packed row lr = RPW*wave + 16*nb + li.
+  int p_row[NB];  // position of the row (INT_MAX past the tile: no key is masked)
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
-    const int lr0 = wave * C::RPW + nb * 16;
-    const int lr = lr0 + li;
+  for (int nb = 0; nb < NB; ++nb) {
+    const int lr = wave * C::RPW + nb * 16 + li;
     p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
-    nb_pmax[nb] = lr0 < tile_rows ? ctx + (it.row_start + min(lr0 + 15, tile_rows - 1)) / g : -1;
   }
   const int p_min = ctx + it.row_start / g;
-  int wave_pmax = -1;  // largest position among the wave's valid rows
-#pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) wave_pmax = max(wave_pmax, nb_pmax[nb]);
 
   // ---- page ids of the keys this item visits -> LDS
   const int page_size = a.page_size;
   const int page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz(page_size) : -1;
-  const int key_lo = it.kv_tile_begin * C::BN;
+  const int kt0 = it.kv_tile_begin;
+  const int n_tiles = it.kv_tile_end - kt0;  // >= 1
+  const int key_lo = kt0 * C::BN;
   const int key_hi = min(it.kv_tile_end * C::BN, rq.kv_len);
   const int key_lo_page = key_lo / page_size;
   const int n_pages = key_hi > key_lo ? (key_hi - 1) / page_size - key_lo_page + 1 : 0;
-  constexpr int kElemBytes = FP8 ? 1 : 2;
-  const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElemBytes;
-  const int64_t page_bytes = token_bytes * page_size;
   for (int i = tid; i < n_pages; i += C::THREADS) {
-    const int64_t id = a.kv_indices[rq.page_start + key_lo_page + i];
-    pg_lds[i] = (id >= 0 && id < a.num_pages) ? id * page_bytes : -1;
+    const int32_t id = a.kv_indices[rq.page_start + key_lo_page + i];
+    pg_lds[i] = (id >= 0 && id < a.num_pages) ? id : -1;
   }
 
   // ---- query rows as the QK^T B operand: lane (lg, li) holds head_dim [32dc + 8lg, +8)
-  bf16x8 qreg[C::NB][C::DC];
+  bf16x8 qreg[NB][C::DC];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int lr = wave * C::RPW + nb * 16 + li;
     const bool valid = lr < tile_rows;
     const int R = it.row_start + lr;
@@ -224,226 +233,330 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       qreg[nb][dc] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // Q and the page ids in registers before any DMA load is issued: a wait for them inside
+  // the loop would also wait for every DMA load in flight
+  wait_vmcnt<0>();
   __syncthreads();  // page table visible
 
-  // ---- staging: this thread moves chunks q = tid + THREADS*i (key q / CH, chunk q % CH)
-  Raw<FP8> kst[PF][C::CPT], vst[PF][C::CPT];
-
-  // Branch-free gather (a branch around each load would keep the compiler from counting
-  // outstanding loads, and it would then wait for every prefetched tile at each LDS store):
-  // a chunk past kv_len, or on a page id outside the pool, reads 16 zero bytes from the
-  // preamble's reserved words instead. When the page size is a power of two no larger than
-  // a KV tile, a thread's page slot and in-page offset are the same for every tile.
+  // ---- gather. Chunk i (0 <= i < NCH) of this thread in every KV tile is a fixed 16-byte
+  // piece of a fixed key row; only the page it sits on changes from tile to tile. A chunk
+  // past kv_len, of a tile outside the item, or on a page id outside the pool reads 16 zero
+  // bytes from the preamble's reserved words instead: the loads never branch, so their
+  // number per tile is fixed.
+  //   bf16: the chunks of one wave's DMA load are the 64 consecutive LDS chunks
+  //         [64 (i WAVES + wave), +64); the global chunk is chosen so that it lands in its
+  //         swizzled slot.
+  //   fp8:  chunk q = tid + THREADS i, loaded to registers, decoded, stored to its slot.
+  constexpr int kElem = FP8 ? 1 : 2;
+  const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElem;
+  const int64_t page_bytes = token_bytes * page_size;
+  constexpr bool pow2_pages = P2;
   const unsigned char* zero16 = reinterpret_cast<const unsigned char*>(pre->reserved);
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k_pool);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v_pool);
-  const bool pow2_pages = page_shift >= 0 && page_size <= C::BN;
-  int kr[C::CPT];          // key row of the tile this thread stages
-  int pg_rel[C::CPT];      // its page, relative to the tile's first page (pow2_pages)
-  int64_t in_page[C::CPT]; // byte offset inside the page: slot, kv head, chunk
+  int krow[C::NCH];        // key row inside the tile
+  int kcol[C::NCH];        // byte offset of the K chunk inside a token's row of the pool
+  int vcol[C::NCH];        // same for V
+  int lds_k[C::NCH];       // fp8: LDS byte offset of the decoded K chunk (V: lds_v)
+  int lds_v[C::NCH];
+  int pg_rel[C::NCH];      // pow2 pages: page of the key row relative to the tile's first
+  int64_t in_page[C::NCH]; // pow2 pages: byte offset of the key row inside its page
 #pragma unroll
-  for (int i = 0; i < C::CPT; ++i) {
-    const int q = tid + C::THREADS * i;
-    kr[i] = q / C::CH;
-    const int64_t chunk_bytes = ((int64_t)kvh * D + (q % C::CH) * 8) * kElemBytes;
-    pg_rel[i] = pow2_pages ? (kr[i] >> page_shift) : 0;
-    in_page[i] = (pow2_pages ? (int64_t)(kr[i] & (page_size - 1)) * token_bytes : 0) + chunk_bytes;
-  }
-  auto load_tile = [&](int slot, int kt) {
-    const int tile_page = pow2_pages ? ((kt * C::BN) >> page_shift) - key_lo_page : 0;
-#pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int j = kt * C::BN + kr[i];
-      int64_t off;
-      if (pow2_pages) {
-        off = pg_lds[tile_page + pg_rel[i]];
-        off = off < 0 ? off : off + in_page[i];
-      } else {
-        const int jj = min(j, rq.kv_len - 1);
-        const int pi = jj / page_size;
-        const int64_t po = pg_lds[pi - key_lo_page];
-        off = po < 0 ? po : po + (int64_t)(jj - pi * page_size) * token_bytes + in_page[i];
-      }
-      const bool ok = j < rq.kv_len && off >= 0;
-      const unsigned char* kp = ok ? kbase + off : zero16;
-      const unsigned char* vp = ok ? vbase + off : zero16;
-      if constexpr (FP8) {
-        kst[slot][i].v = *reinterpret_cast<const u32x2*>(kp);
-        vst[slot][i].v = *reinterpret_cast<const u32x2*>(vp);
-      } else {
-        kst[slot][i].v = *reinterpret_cast<const u32x4*>(kp);
-        vst[slot][i].v = *reinterpret_cast<const u32x4*>(vp);
-      }
+  for (int i = 0; i < C::NCH; ++i) {
+    int c_k, c_v;
+    if constexpr (FP8) {
+      const int q = tid + C::THREADS * i;
+      krow[i] = q / C::CH;
+      c_k = c_v = q % C::CH;
+      lds_k[i] = chunk_off<C::ROW_BYTES>(krow[i], c_k);
+      lds_v[i] = chunk_off_v<C::ROW_BYTES>(krow[i], c_v);
+    } else {
+      const int q = (i * C::WAVES + wave) * 64 + lane;
+      krow[i] = q / C::CH;
+      const int slot = q % C::CH;
+      c_k = slot ^ (krow[i] & 15);         // chunk_off(key, c_k) == 16 q
+      c_v = slot ^ ((krow[i] & 7) << 1);   // chunk_off_v(key, c_v) == 16 q
+      lds_k[i] = lds_v[i] = 0;
     }
+    kcol[i] = (kvh * D + c_k * 8) * kElem;
+    vcol[i] = (kvh * D + c_v * 8) * kElem;
+    pg_rel[i] = pow2_pages ? (krow[i] >> page_shift) : 0;
+    in_page[i] = pow2_pages ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
+  }
+  // source of chunk i of item tile t of one tensor
+  auto chunk_src = [&](const unsigned char* base, int col, int t, int i) -> const unsigned char* {
+    const int kt = kt0 + min(max(t, 0), n_tiles - 1);
+    const int key = kt * C::BN + krow[i];
+    int64_t pid, inpg;
+    if constexpr (pow2_pages) {
+      pid = pg_lds[((kt * C::BN) >> page_shift) - key_lo_page + pg_rel[i]];
+      inpg = in_page[i];
+    } else {
+      const int kk = min(key, rq.kv_len - 1);
+      const int pi = kk / page_size;
+      pid = pg_lds[pi - key_lo_page];
+      inpg = (int64_t)(kk - pi * page_size) * token_bytes;
+    }
+    const bool ok = t >= 0 && t < n_tiles && key < rq.kv_len && pid >= 0;
+    return ok ? base + (pid * page_bytes + inpg + col) : zero16;
   };
 
-  auto store_tile = [&](int slot, int stage) {
-    unsigned char* kt_lds = smem + stage * C::STAGE_BYTES;
-    unsigned char* vt_lds = kt_lds + C::TILE_BYTES;
+  // LDS: K buffers 0..NBUF-1, then V buffers 0..NBUF-1; tile t uses buffers t % NBUF.
+  // Load group t brings K(t + NBUF) and V(t + NBUF - 2). It is issued in iteration t and
+  // complete before the barrier that ends iteration t + 2; iteration t reads K(t + 1) and
+  // V(t - 1). K(t + NBUF) replaces K(t), last read in iteration t - 1 (K(0): in the
+  // prologue, which ends with a barrier for it), and V(t + NBUF - 2) replaces V(t - 2), last
+  // read in iteration t - 1.
+  static_assert(C::NBUF == 4, "the schedule below assumes four buffers");
+  const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the dynamic block
+  auto dma_tile = [&](bool v, int t) {
+    const uint32_t buf = lds0 + (uint32_t)(((v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES);
 #pragma unroll
-    for (int i = 0; i < C::CPT; ++i) {
-      const int q = tid + C::THREADS * i;
-      const int off = chunk_off<C::ROW_BYTES>(q / C::CH, q % C::CH);
-      const int off_v = chunk_off_v<C::ROW_BYTES>(q / C::CH, q % C::CH);
-      if constexpr (FP8) {
-        *reinterpret_cast<u32x4*>(kt_lds + off) = dequant8(kst[slot][i].v, a.k_scale);
-        *reinterpret_cast<u32x4*>(vt_lds + off_v) = dequant8(vst[slot][i].v, a.v_scale);
-      } else {
-        *reinterpret_cast<u32x4*>(kt_lds + off) = kst[slot][i].v;
-        *reinterpret_cast<u32x4*>(vt_lds + off_v) = vst[slot][i].v;
-      }
+    for (int i = 0; i < C::NCH; ++i)
+      dma16(chunk_src(v ? vbase : kbase, v ? vcol[i] : kcol[i], t, i), buf + (uint32_t)((i * C::WAVES + wave) * 1024));
+  };
+  u32x2 kreg[C::NCH], vreg[C::NCH];  // fp8 staging of one load group
+  auto fp8_load = [&](int tk, int tv) {
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      kreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(kbase, kcol[i], tk, i));
+      vreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(vbase, vcol[i], tv, i));
     }
   };
+  auto fp8_store = [&](int tk, int tv) {
+    unsigned char* kb = smem + (tk & (C::NBUF - 1)) * C::TILE_BYTES;
+    unsigned char* vb = smem + (C::NBUF + (tv & (C::NBUF - 1))) * C::TILE_BYTES;
+#pragma unroll
+    for (int i = 0; i < C::NCH; ++i) {
+      *reinterpret_cast<u32x4*>(kb + lds_k[i]) = dequant8(kreg[i], a.k_scale);
+      *reinterpret_cast<u32x4*>(vb + lds_v[i]) = dequant8(vreg[i], a.v_scale);
+    }
+  };
+  auto issue_group = [&](int t) {  // bf16: DMA of load group t
+    dma_tile(false, t + C::NBUF);
+    dma_tile(true, t + C::NBUF - 2);
+  };
+  constexpr int kGroupLoads = 2 * C::NCH;
 
   // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
-  float m_sc[C::NB], l_sum[C::NB];  // reference max (scaled, base 2) and running sum per row
-  f32x4 acc[C::DB][C::NB];
+  float m_sc[NB], l_sum[NB];  // reference max (scaled, base 2) and running sum per row
+  f32x4 acc[C::DB][NB];
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     m_sc[nb] = -INFINITY;
     l_sum[nb] = 0.f;
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const int kt0 = it.kv_tile_begin;
-  const int kt1 = it.kv_tile_end;
-  // Tile T lives in register slot (T - kt0) % PF until it is stored into LDS stage
-  // (T - kt0) % NS. Prologue: tiles kt0 .. kt0+PF-1 in flight, tile kt0 stored, its slot
-  // refilled with tile kt0+PF. Loads are issued unconditionally (tile numbers past the end
-  // re-read the last tile, which is never stored): with every load on every path the
-  // compiler can wait for exactly one tile at each store instead of for all of them.
-  const int kt_last = kt1 - 1;
+  // S^T = K Q^T for tile t
+  auto qk = [&](f32x4 (&s)[C::KB][NB], int t) {
+    const unsigned char* k_lds = smem + (t & (C::NBUF - 1)) * C::TILE_BYTES;
 #pragma unroll
-  for (int s = 0; s < PF; ++s) load_tile(s, min(kt0 + s, kt_last));
-  store_tile(0, 0);
-  load_tile(0, min(kt0 + PF, kt_last));
-  __syncthreads();
-
-  // Per tile: store tile kt+1 into its stage (that stage was last read two tiles ago, before
-  // the previous barrier), refill the freed slot with tile kt+1+PF, compute tile kt, barrier.
-  // Unrolled by PF so every register slot index is a compile-time constant.
-  for (int base = kt0; base < kt1; base += PF) {
+    for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
-    for (int u = 0; u < PF; ++u) {
-      const int kt = base + u;
-      const bool live = kt < kt1;  // the last unrolled group may run past the item's tiles
-      const int rel = kt - kt0;
-      if (kt + 1 < kt1) store_tile((u + 1) % PF, (rel + 1) % C::NS);
-      load_tile((u + 1) % PF, min(kt + 1 + PF, kt_last));
-
-      const unsigned char* k_lds = smem + (rel % C::NS) * C::STAGE_BYTES;
-      const unsigned char* v_lds = k_lds + C::TILE_BYTES;
-      const int key0 = kt * C::BN;
-      const bool diag = key0 + C::BN - 1 > p_min;
-
-      // The wave has work in this tile when one of its valid rows reaches key0. Its blocks
-      // then all run the same straight-line code: for a row that does not reach key0 every
-      // score is masked, alpha = 1 and P = 0, so the tile changes none of its state.
-      if (live && wave_pmax >= key0) {
-        // S^T = K Q^T
-        f32x4 s[C::KB][C::NB];
+      for (int nb = 0; nb < NB; ++nb) s[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // every s[kb][nb] accumulates head_dim chunks dc = 0, 1, ... in that order
 #pragma unroll
-        for (int kb = 0; kb < C::KB; ++kb) {
+    for (int dc = 0; dc < C::DC; ++dc) {
 #pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) s[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int kb = 0; kb < C::KB; ++kb) {
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + chunk_off<C::ROW_BYTES>(kb * 16 + li, dc * 4 + lg));
 #pragma unroll
-          for (int dc = 0; dc < C::DC; ++dc) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + chunk_off<C::ROW_BYTES>(kb * 16 + li, dc * 4 + lg));
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-              s[kb][nb] = mfma16(ka, qreg[nb][dc], s[kb][nb]);
-          }
-        }
-        // causal mask: s[kb][nb][j] holds key key0 + 16kb + 4lg + j of row p_row[nb]
-        if (diag) {
-#pragma unroll
-          for (int nb = 0; nb < C::NB; ++nb) {
-            const int thr = p_row[nb] - key0 - 4 * lg;  // masked iff 16kb + j > thr
-#pragma unroll
-            for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-              for (int j = 0; j < 4; ++j) s[kb][nb][j] = (kb * 16 + j > thr) ? -INFINITY : s[kb][nb][j];
-          }
-        }
-        // online softmax, per 16-row block
-        bf16x8 pb[C::KC][C::NB];
-#pragma unroll
-        for (int nb = 0; nb < C::NB; ++nb) {
-          float mx = s[0][nb][0];
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kb][nb][j]);
-          mx = row_max4(mx);
-          // The reference max moves only when this tile's max exceeds it by more than
-          // kRebase (and on the row's first keys); otherwise P_j <= 2^kRebase and O, l keep
-          // their scale. Same softmax, and O is rescaled only on the rare rebase.
-          const float mx_sc = mx * c;
-          const bool rebase = mx_sc > m_sc[nb] + kRebase;
-          const float m_use = rebase ? mx_sc : m_sc[nb];
-          const float alpha = rebase ? __builtin_amdgcn_exp2f(m_sc[nb] - m_use) : 1.f;
-          m_sc[nb] = m_use;
-          float pv[C::KB][4];
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) pv[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][nb][j], c, -m_use));
-          // row sum: pairs within each 4-key group, then a pairwise tree over the groups
-          float t[C::KB];
-#pragma unroll
-          for (int kb = 0; kb < C::KB; ++kb) t[kb] = (pv[kb][0] + pv[kb][1]) + (pv[kb][2] + pv[kb][3]);
-#pragma unroll
-          for (int w = C::KB / 2; w >= 1; w >>= 1)
-#pragma unroll
-            for (int i = 0; i < w; ++i) t[i] = t[2 * i] + t[2 * i + 1];
-          const float rs = row_sum4(t[0]);
-          l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha, rs);
-          if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha;
-          }
-          // P^T as the PV B operand: k = 8lg + t is key 32kc + 16(t/4) + 4lg + t%4
-#pragma unroll
-          for (int kc = 0; kc < C::KC; ++kc) {
-            const u32x4 w4 = u32x4{pack_bf16x2(pv[2 * kc][0], pv[2 * kc][1]),
-                                   pack_bf16x2(pv[2 * kc][2], pv[2 * kc][3]),
-                                   pack_bf16x2(pv[2 * kc + 1][0], pv[2 * kc + 1][1]),
-                                   pack_bf16x2(pv[2 * kc + 1][2], pv[2 * kc + 1][3])};
-            pb[kc][nb] = __builtin_bit_cast(bf16x8, w4);
-          }
-        }
-        // O^T += V^T P^T. V^T comes transposed from the natural layout: lane (lg, r) of read h
-        // points at key 32kc + 16h + 4lg + r/4, head_dim 16db + 4(r%4), and receives
-        // V[32kc + 16h + 4lg + j][16db + li] for j = 0..3 -- the A operand's k = 8lg + 4h + j.
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db) {
-#pragma unroll
-          for (int kc = 0; kc < C::KC; ++kc) {
-            s16x4 hv[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
-              const int e = db * 16 + 4 * (li & 3);
-              const unsigned char* addr = v_lds + chunk_off_v<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
-              hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
-            }
-            const s16x8 v8 = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
-            const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-            for (int nb = 0; nb < C::NB; ++nb)
-              acc[db][nb] = mfma16(va, pb[kc][nb], acc[db][nb]);
-          }
-        }
+        for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma16(ka, qreg[nb][dc], s[kb][nb]);
       }
-      __syncthreads();
     }
+  };
+
+  // causal mask of tile t: s[kb][nb][j] holds key key0 + 16kb + 4lg + j of row p_row[nb]
+  auto mask = [&](f32x4 (&s)[C::KB][NB], int t) {
+    const int key0 = (kt0 + t) * C::BN;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int thr = p_row[nb] - key0 - 4 * lg;  // masked iff 16kb + j > thr
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) s[kb][nb][j] = (kb * 16 + j > thr) ? -INFINITY : s[kb][nb][j];
+    }
+  };
+
+  // online softmax of one tile: P^T into pb, alpha per row block; returns whether some row
+  // of the wave moved its reference (then O must be rescaled by alpha, see rescale)
+  auto softmax = [&](f32x4 (&s)[C::KB][NB], bf16x8 (&pb)[C::KC][NB], float (&alpha)[NB]) -> bool {
+    bool moved = false;
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      float mx = s[0][nb][0];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kb][nb][j]);
+      mx = row_max4(mx);
+      // The reference max moves only when this tile's max exceeds it by more than kRebase
+      // (and on the row's first keys); otherwise P_j <= 2^kRebase and O, l keep their scale.
+      const float mx_sc = mx * c;
+      const bool rebase = mx_sc > m_sc[nb] + kRebase;
+      const float m_use = rebase ? mx_sc : m_sc[nb];
+      alpha[nb] = rebase ? __builtin_amdgcn_exp2f(m_sc[nb] - m_use) : 1.f;
+      m_sc[nb] = m_use;
+      moved = moved || rebase;
+      float pv[C::KB][4];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) pv[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][nb][j], c, -m_use));
+      // row sum: pairs within each 4-key group, then a pairwise tree over the groups
+      float ts[C::KB];
+#pragma unroll
+      for (int kb = 0; kb < C::KB; ++kb) ts[kb] = (pv[kb][0] + pv[kb][1]) + (pv[kb][2] + pv[kb][3]);
+#pragma unroll
+      for (int h = C::KB / 2; h >= 1; h >>= 1)
+#pragma unroll
+        for (int i = 0; i < h; ++i) ts[i] = ts[2 * i] + ts[2 * i + 1];
+      const float rs = row_sum4(ts[0]);
+      l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha[nb], rs);
+      if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha[nb];
+      }
+      // P^T as the PV B operand: k = 8lg + i is key 32kc + 16(i/4) + 4lg + i%4
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) {
+        const u32x4 w4 = u32x4{pack_bf16x2(pv[2 * kc][0], pv[2 * kc][1]),
+                               pack_bf16x2(pv[2 * kc][2], pv[2 * kc][3]),
+                               pack_bf16x2(pv[2 * kc + 1][0], pv[2 * kc + 1][1]),
+                               pack_bf16x2(pv[2 * kc + 1][2], pv[2 * kc + 1][3])};
+        pb[kc][nb] = __builtin_bit_cast(bf16x8, w4);
+      }
+    }
+    return __any(moved);
+  };
+  // O = alpha O (alpha = 1 exactly for the rows that kept their reference)
+  auto rescale = [&](const float (&alpha)[NB]) {
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb)
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha[nb];
+  };
+
+  // O^T += V^T P^T for tile t. V^T comes transposed from the natural layout: lane (lg, r) of
+  // read h points at key 32kc + 16h + 4lg + r/4, head_dim 16db + 4(r%4), and receives
+  // V[32kc + 16h + 4lg + j][16db + li] for j = 0..3 -- the A operand's k = 8lg + 4h + j.
+  auto pv_acc = [&](const bf16x8 (&pb)[C::KC][NB], int t) {
+    const unsigned char* v_lds = smem + (C::NBUF + (t & (C::NBUF - 1))) * C::TILE_BYTES;
+    // every acc[db][nb] accumulates key chunks kc = 0, 1, ... in that order
+#pragma unroll
+    for (int kc = 0; kc < C::KC; ++kc) {
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) {
+        s16x4 hv[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
+          const int e = db * 16 + 4 * (li & 3);
+          const unsigned char* addr = v_lds + chunk_off_v<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
+          hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
+        }
+        const s16x8 v8 = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
+#pragma unroll
+        for (int nb = 0; nb < NB; ++nb) acc[db][nb] = mfma16(va, pb[kc][nb], acc[db][nb]);
+      }
+    }
+  };
+
+  // Instruction order inside the two straight-line blocks of an iteration (the scheduler's
+  // groups: 0x008 MFMA, 0x402 vector ALU incl. transcendental, 0x100 LDS read). PV(t-1) with
+  // softmax(t): each step's V^T reads go two steps ahead of their MFMAs and the softmax
+  // arithmetic fills the gaps between MFMAs. QK^T(t+1): K reads two steps ahead.
+  constexpr int kSteps = C::DB * C::KC;  // PV steps: 2 V^T reads, NB MFMAs each
+  static_assert(kSteps == C::DC * C::KB, "QK^T has as many steps (1 K read, NB MFMAs)");
+  auto sched_pv_softmax = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+#pragma unroll
+      for (int m = 0; m < NB; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+        if (m == 0 && st + 2 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+    }
+  };
+  auto sched_qk = [&]() {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+    for (int st = 0; st < kSteps; ++st) {
+      if (st + 2 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+    }
+  };
+
+  // ---- schedule: iteration t = 0 .. n_tiles-1 issues load group t, then (waves with rows)
+  // masks S(t) on a diagonal tile, runs PV(t-1) and softmax(t) -- independent matrix-core and
+  // vector work, so the wave issues softmax arithmetic while its MFMAs run -- then QK^T(t+1)
+  // into the same score registers, and ends with a barrier once load group t-2 has landed.
+  // PV(n_tiles-1) follows the loop. Per row this is the plain sequence over tiles:
+  // O = alpha(t) O, then O += PV(t). QK^T of the tile past the item reads a zero-filled
+  // buffer and is discarded; PV(-1) adds V(-1) P(-1) = 0 * 0 (both zero-filled).
+  f32x4 s[C::KB][NB];
+  bf16x8 p0[C::KC][NB], p1[C::KC][NB];
+#pragma unroll
+  for (int kc = 0; kc < C::KC; ++kc)
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) p0[kc][nb] = p1[kc][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+
+  if constexpr (FP8) {
+#pragma unroll
+    for (int t = -C::NBUF; t < -1; ++t) {
+      fp8_load(t + C::NBUF, t + C::NBUF - 2);
+      fp8_store(t + C::NBUF, t + C::NBUF - 2);
+    }
+    fp8_load(C::NBUF - 1, C::NBUF - 3);  // group -1, stored in iteration 0
+  } else {
+#pragma unroll
+    for (int t = -C::NBUF; t < 0; ++t) issue_group(t);
+    wait_vmcnt<2 * kGroupLoads>();  // groups -4 and -3 landed: K(0), K(1), V(-1)
   }
+  __syncthreads();
+  if (has_rows) qk(s, 0);
+  // load group 0 overwrites K(0): every wave's QK^T(0) must be done with it first
+  if constexpr (!FP8) __syncthreads();
+
+  // p_prv/p_cur alternate between the two register sets (no copies)
+  auto iteration = [&](int t, bf16x8 (&p_prv)[C::KC][NB], bf16x8 (&p_cur)[C::KC][NB]) {
+    if constexpr (FP8) {
+      fp8_store(t + C::NBUF - 1, t + C::NBUF - 3);  // group t-1
+      fp8_load(t + C::NBUF, t + C::NBUF - 2);       // group t
+    } else {
+      issue_group(t);
+    }
+    if (has_rows) {
+      if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
+      float alpha[NB];
+      pv_acc(p_prv, t - 1);
+      softmax(s, p_cur, alpha);
+      qk(s, t + 1);
+    }
+    if constexpr (!FP8) wait_vmcnt<2 * kGroupLoads>();  // group t-2 landed
+    __syncthreads();
+  };
+  for (int t = 0; t < n_tiles; t += 2) {
+    iteration(t, p0, p1);
+    if (t + 1 < n_tiles) iteration(t + 1, p1, p0);
+  }
+  if (has_rows) {
+    if (n_tiles & 1) pv_acc(p1, n_tiles - 1);
+    else pv_acc(p0, n_tiles - 1);
+  }
+  wait_vmcnt<0>();  // no load may outlive the workgroup (a DMA load would land in LDS)
 
   // ---- epilogue: lane holds O^T[d = 16db + 4lg + j][row 16nb + li]
+  if (!has_rows) return;
 #pragma unroll
-  for (int nb = 0; nb < C::NB; ++nb) {
+  for (int nb = 0; nb < NB; ++nb) {
     const int lr = wave * C::RPW + nb * 16 + li;
     const int p = p_row[nb];
     if (lr >= tile_rows || p < split_key0) continue;  // not a row of this split
@@ -461,7 +574,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
                   pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
       if (lg == 0) a.lse[orow] = lse2 * kLn2;
     } else {
-      const int64_t slot = partial_slot(it.slot_base, it.tile_splits, kvh, it.split, lr, C::BM);
+      const int64_t slot = partial_slot(it.slot_base, it.tile_splits, kvh, it.split, lr, C::PLAN_BM);
       float* pp = a.part_o + slot * D + 4 * lg;
 #pragma unroll
       for (int db = 0; db < C::DB; ++db)
@@ -472,29 +585,45 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   }
 }
 
-template <int D, bool FP8, int PF>
+template <int D, bool FP8, int NB, bool P2>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  using C = Cfg<D>;
-  const size_t lds = (size_t)C::LDS_BYTES + (size_t)a.page_slots * 8;
+  using C = Geo<D, NB>;
+  // page-id table: the item's pages plus one tile's worth of slack for the last tile's
+  // lookups past kv_len (their chunks read the zero chunk)
+  const size_t lds = (size_t)C::LDS_BYTES + ((size_t)a.page_slots + C::BN) * 4;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, PF>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, P2>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
   }
-  dim3 grid((unsigned)a.num_items, (unsigned)a.num_kv_heads);
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, PF>), grid, dim3(C::THREADS), lds, stream, a);
+  dim3 grid((unsigned)(a.num_items * a.num_kv_heads));
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, P2>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
+}
+
+template <int D, int NB>
+hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
+  const int P = a.page_size;
+  const bool p2 = (P & (P - 1)) == 0 && P <= block_n_for(D);
+  if (fp8) return p2 ? launch_one<D, true, NB, true>(a, stream) : launch_one<D, true, NB, false>(a, stream);
+  return p2 ? launch_one<D, false, NB, true>(a, stream) : launch_one<D, false, NB, false>(a, stream);
+}
+
+template <int D>
+hipError_t launch_d(const PrefillArgs& a, bool fp8, bool narrow, hipStream_t stream) {
+  constexpr int kWide = rows_per_wave_for(D) / 16;
+  return narrow ? launch_nb<D, 1>(a, fp8, stream) : launch_nb<D, kWide>(a, fp8, stream);
 }
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool narrow, hipStream_t stream) {
   const bool fp8 = kv_dtype == 1;
-  if (head_dim == 128) return fp8 ? launch_one<128, true, 2>(a, stream) : launch_one<128, false, 2>(a, stream);
-  if (head_dim == 256) return fp8 ? launch_one<256, true, 2>(a, stream) : launch_one<256, false, 2>(a, stream);
+  if (head_dim == 128) return launch_d<128>(a, fp8, narrow, stream);
+  if (head_dim == 256) return launch_d<256>(a, fp8, narrow, stream);
   return hipErrorInvalidValue;
 }
 
