@@ -113,6 +113,7 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   a.group = plan->group;
   a.page_size = plan->cfg.page_size;
   a.page_slots = plan->page_slots;
+  a.item_offset = plan->item_offset;
   a.scale_log2 = plan->scale_log2;
   a.k_scale = plan->cfg.k_scale;
   a.v_scale = plan->cfg.v_scale;

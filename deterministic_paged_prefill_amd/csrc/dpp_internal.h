@@ -68,7 +68,8 @@ struct RequestDesc {
   int32_t kv_len;
 };
 
-// One (q tile, KV split) unit of the prefill kernel, for every kv head (grid.y).
+// One (q tile, KV split) unit of the prefill kernel, run once per kv head. It carries a copy
+// of its request's descriptor, so a workgroup reads one record before it can start loading.
 struct PrefillItem {
   int32_t request;
   int32_t row_start;     // first packed row of the tile (multiple of block_m_for(head_dim))
@@ -77,8 +78,12 @@ struct PrefillItem {
   int32_t kv_tile_begin; // first KV tile (absolute, units of block_n_for(head_dim))
   int32_t kv_tile_end;   // one past the last KV tile this item visits
   int32_t slot_base;     // first partial slot of the tile in this pass, -1 if S_t == 1
-  int32_t pad;
+  int32_t pad0;
+  RequestDesc req;       // the request's descriptor
+  int32_t pad1[4];
 };
+static_assert(sizeof(PrefillItem) == 64, "item record is 16 words");
+constexpr int kItemWords = 16;
 
 // One q tile whose rows span several splits: merge its partials.
 struct MergeItem {
@@ -122,6 +127,7 @@ struct PrefillArgs {
   float* part_lse2;         // [slots] (base-2 log-sum-exp of the split)
   int64_t num_pages;
   uint32_t plan_id;
+  int32_t item_offset;      // word offset of the item records in the header
   int32_t item_begin;       // first item of this pass
   int32_t num_items;        // items in this pass
   int32_t num_qo_heads;

@@ -137,7 +137,7 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     n_items += t.splits;
     n_merges += t.splits > 1 ? 1 : 0;
   }
-  const int64_t words = kHeaderWords + 4 * (int64_t)batch_size + 8 * n_items + 4 * n_merges;
+  const int64_t words = kHeaderWords + 4 * (int64_t)batch_size + kItemWords * n_items + 4 * n_merges;
   if (n_items > std::numeric_limits<int32_t>::max() / 2 / c.num_kv_heads ||
       words > std::numeric_limits<int32_t>::max() / 2)
     return fail(DPP_ERR_UNSUPPORTED, "batch too large for one plan");
@@ -211,6 +211,7 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
         it.kv_tile_begin = s * tiles_per_split;
         it.kv_tile_end = (int32_t)std::min<int64_t>((int64_t)(s + 1) * tiles_per_split, last_tile + 1);
         it.slot_base = (int32_t)t.slot_base;
+        it.req = rq;
         const int64_t key_lo = (int64_t)it.kv_tile_begin * block_n;
         const int64_t key_hi = std::min<int64_t>((int64_t)it.kv_tile_end * block_n, rq.kv_len);
         if (key_hi > key_lo) max_page_span = std::max(max_page_span, (key_hi - 1) / P - key_lo / P + 1);
@@ -255,7 +256,7 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   pre.num_merges = (int32_t)n_merges;
   pre.request_offset = kHeaderWords;
   pre.item_offset = kHeaderWords + 4 * batch_size;
-  pre.merge_offset = pre.item_offset + 8 * (int32_t)n_items;
+  pre.merge_offset = pre.item_offset + kItemWords * (int32_t)n_items;
   {
     // ids differ between plans of one process; mixing in the address makes a header left
     // behind by another process unlikely to match either
@@ -265,6 +266,7 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     plan->plan_id = pre.plan_id;
   }
   std::memcpy(plan->header.data(), &pre, sizeof pre);
+  plan->item_offset = pre.item_offset;
   if (batch_size > 0)
     std::memcpy(plan->header.data() + pre.request_offset, reqs.data(), reqs.size() * sizeof(RequestDesc));
   if (!items.empty())

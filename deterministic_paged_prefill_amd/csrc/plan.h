@@ -36,6 +36,7 @@ struct dpp_plan {
   size_t partial_lse_offset = 0;
   size_t workspace_bytes = 0;
   int32_t page_slots = 0;         // LDS page-id entries one item may need
+  int32_t item_offset = 0;        // word offset of the item records in the header
   uint32_t plan_id = 0;           // stamped into the work list
 
   // Pinned host copy of `header`, created on first dpp_run (plan creation stays HIP-free).

@@ -56,6 +56,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.693147180559945309417f;
 // Rebase threshold of the online softmax's reference max, in log2 units (P_j <= 2^8).
 constexpr float kRebase = 8.0f;
+// LDS operand reads of QK^T and PV run this many MFMA steps ahead of their use.
+constexpr int kAhead = 3;
 
 template <int D, int NB>
 struct Geo {
@@ -73,6 +75,7 @@ struct Geo {
   static constexpr int DB = D / 16;                // 16-wide head_dim blocks (PV M blocks)
   static constexpr int KC = BN / 32;               // 32-key chunks (PV k-steps)
   static constexpr int NCH = BN * CH / THREADS;    // 16-byte chunks per thread per tensor per tile
+  static constexpr int KPI = 64 * 16 / ROW_BYTES;  // key rows one wave-wide DMA load covers
   static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
   static_assert(NCH * THREADS == BN * CH, "the threads cover a tile");
   static_assert(NCH * 64 * WAVES * 16 == TILE_BYTES, "one DMA load per wave moves 1 KiB");
@@ -155,6 +158,23 @@ __device__ inline void dma16(const void* gaddr, uint32_t lds_base) {
                : "memory");
 }
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor (stride 0: num_records counts bytes) over [base, base + bytes); a
+// load at an offset past `bytes` returns zeros.
+__device__ inline i32x4 buffer_rsrc(uint64_t base, uint32_t bytes) {
+  return i32x4{(int)(uint32_t)base, (int)((uint32_t)(base >> 32) & 0xFFFFu), (int)bytes, 0x00020000};
+}
+
+// LDS-DMA through a buffer descriptor: lane l fetches 16 bytes at descriptor offset
+// voff (zeros past num_records) and they land at LDS byte address lds_base + 16 l.
+__device__ inline void dma16_buf(int voff, i32x4 rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "memory");
+}
+
 // s_waitcnt vmcnt(N), no wait on the other counters.
 template <int N>
 __device__ inline void wait_vmcnt() {
@@ -162,13 +182,24 @@ __device__ inline void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
 
-// NB: 16-row blocks per wave. P2: page_size is a power of two no larger than a KV tile, so a
-// chunk's page within its tile and its offset in that page are the same for every tile.
-template <int D, bool FP8, int NB, bool P2>
+// How a chunk's global address is found (a template parameter, fixed per launch):
+//   kPagesGeneral  any page size: per-lane division by page_size
+//   kPagesPow2     page_size a power of two no larger than a KV tile: a chunk's page within
+//                  its tile and its offset in that page are the same for every tile
+//   kPagesScalar   bf16, page_size a power of two holding whole DMA loads (a multiple of the
+//                  keys one load covers): the page of a load is uniform, its address is built
+//                  in scalar registers as a buffer descriptor whose size ends at kv_len (the
+//                  hardware returns zeros past it)
+constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2;
+
+// NB: 16-row blocks per wave.
+template <int D, bool FP8, int NB, int MODE>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
   using C = Geo<D, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + C::LDS_BYTES);  // page ids, -1 = bad id
+  // page table of the item: page ids (-1 = bad id), or in scalar mode the pages' byte offsets
+  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + C::LDS_BYTES);
+  int64_t* pg_off = reinterpret_cast<int64_t*>(smem + C::LDS_BYTES);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -179,11 +210,13 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int w = xcd_chunked(blockIdx.x, a.num_items * a.num_kv_heads);
   const int kvh = w / a.num_items;
 
+  // The item record (with its request's descriptor) and the preamble are read together; the
+  // record lies inside the workspace whatever the header holds.
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
-  if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
   const PrefillItem it =
-      reinterpret_cast<const PrefillItem*>(a.header + pre->item_offset)[a.item_begin + (w - kvh * a.num_items)];
-  const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[it.request];
+      reinterpret_cast<const PrefillItem*>(a.header + a.item_offset)[a.item_begin + (w - kvh * a.num_items)];
+  if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
+  const RequestDesc rq = it.req;
 
   const int g = a.group;
   const int tile_rows = min(C::PLAN_BM, rq.qo_len * g - it.row_start);
@@ -213,7 +246,11 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int n_pages = key_hi > key_lo ? (key_hi - 1) / page_size - key_lo_page + 1 : 0;
   for (int i = tid; i < n_pages; i += C::THREADS) {
     const int32_t id = a.kv_indices[rq.page_start + key_lo_page + i];
-    pg_lds[i] = (id >= 0 && id < a.num_pages) ? id : -1;
+    const bool good = id >= 0 && id < a.num_pages;
+    if constexpr (MODE == kPagesScalar)
+      pg_off[i] = good ? (int64_t)id * ((int64_t)a.num_kv_heads * D * 2 * page_size) : -1;
+    else
+      pg_lds[i] = good ? id : -1;
   }
 
   // ---- query rows as the QK^T B operand: lane (lg, li) holds head_dim [32dc + 8lg, +8)
@@ -250,19 +287,31 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   constexpr int kElem = FP8 ? 1 : 2;
   const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElem;
   const int64_t page_bytes = token_bytes * page_size;
-  constexpr bool pow2_pages = P2;
+  constexpr bool pow2_pages = MODE != kPagesGeneral;
+  static_assert(!(FP8 && MODE == kPagesScalar), "fp8 stages through registers");
+  // Two-group schedule (see below): bf16 wide tiles with two waves per SIMD.
+  constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
+  // The narrow instantiation's computing wave is wave 0 alone: with eight waves, waves 4-7
+  // issue all of its DMA loads. Otherwise every wave issues its share.
+  constexpr int kIssuer0 = (!FP8 && NB == 1 && C::WAVES == 8) ? 4 : 0;
+  constexpr int IW = C::WAVES - kIssuer0;                 // waves that issue DMA loads
+  const int iw = wave - kIssuer0;                         // this wave's index among them
+  const bool issuer = iw >= 0;
+  constexpr int NL = C::TILE_BYTES / (IW * 1024);         // their loads per tensor per tile
+  constexpr int NCHT = FP8 ? C::NCH : NL;                 // chunks per thread per tensor per tile
+  constexpr int KA = kPP ? 3 : C::NBUF;                   // load group t brings K(t + KA), V(t + 2)
   const unsigned char* zero16 = reinterpret_cast<const unsigned char*>(pre->reserved);
   const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k_pool);
   const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v_pool);
-  int krow[C::NCH];        // key row inside the tile
-  int kcol[C::NCH];        // byte offset of the K chunk inside a token's row of the pool
-  int vcol[C::NCH];        // same for V
-  int lds_k[C::NCH];       // fp8: LDS byte offset of the decoded K chunk (V: lds_v)
-  int lds_v[C::NCH];
-  int pg_rel[C::NCH];      // pow2 pages: page of the key row relative to the tile's first
-  int64_t in_page[C::NCH]; // pow2 pages: byte offset of the key row inside its page
+  int krow[NCHT];        // key row inside the tile
+  int kcol[NCHT];        // byte offset of the K chunk inside a token's row of the pool
+  int vcol[NCHT];        // same for V
+  int lds_k[NCHT];       // fp8: LDS byte offset of the decoded K chunk (V: lds_v)
+  int lds_v[NCHT];
+  int pg_rel[NCHT];      // pow2 pages: page of the key row relative to the tile's first
+  int64_t in_page[NCHT]; // pow2 pages: byte offset of the key row inside its page
 #pragma unroll
-  for (int i = 0; i < C::NCH; ++i) {
+  for (int i = 0; i < NCHT; ++i) {
     int c_k, c_v;
     if constexpr (FP8) {
       const int q = tid + C::THREADS * i;
@@ -271,7 +320,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       lds_k[i] = chunk_off<C::ROW_BYTES>(krow[i], c_k);
       lds_v[i] = chunk_off_v<C::ROW_BYTES>(krow[i], c_v);
     } else {
-      const int q = (i * C::WAVES + wave) * 64 + lane;
+      const int q = (i * IW + iw) * 64 + lane;
       krow[i] = q / C::CH;
       const int slot = q % C::CH;
       c_k = slot ^ (krow[i] & 15);         // chunk_off(key, c_k) == 16 q
@@ -280,15 +329,22 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
     kcol[i] = (kvh * D + c_k * 8) * kElem;
     vcol[i] = (kvh * D + c_v * 8) * kElem;
-    pg_rel[i] = pow2_pages ? (krow[i] >> page_shift) : 0;
-    in_page[i] = pow2_pages ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
+    pg_rel[i] = MODE == kPagesPow2 ? (krow[i] >> page_shift) : 0;
+    in_page[i] = MODE == kPagesPow2 ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
+  }
+  // scalar pages: byte offset of the lane's chunk from its load's first key row
+  int voff_k[NCHT], voff_v[NCHT];
+#pragma unroll
+  for (int i = 0; i < NCHT; ++i) {
+    voff_k[i] = (int)((krow[i] % C::KPI) * token_bytes) + kcol[i];
+    voff_v[i] = (int)((krow[i] % C::KPI) * token_bytes) + vcol[i];
   }
   // source of chunk i of item tile t of one tensor
   auto chunk_src = [&](const unsigned char* base, int col, int t, int i) -> const unsigned char* {
     const int kt = kt0 + min(max(t, 0), n_tiles - 1);
     const int key = kt * C::BN + krow[i];
     int64_t pid, inpg;
-    if constexpr (pow2_pages) {
+    if constexpr (MODE == kPagesPow2) {
       pid = pg_lds[((kt * C::BN) >> page_shift) - key_lo_page + pg_rel[i]];
       inpg = in_page[i];
     } else {
@@ -311,9 +367,30 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the dynamic block
   auto dma_tile = [&](bool v, int t) {
     const uint32_t buf = lds0 + (uint32_t)(((v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES);
+    const unsigned char* base = v ? vbase : kbase;
+    if constexpr (MODE == kPagesScalar) {
+      // scalar pages are issued by issue_group_scalar
+    } else if constexpr (pow2_pages) {
+      // all page ids first (one LDS round trip), then selects: no branch per chunk
+      const bool tile_ok = t >= 0 && t < n_tiles;
+      const int kt = kt0 + min(max(t, 0), n_tiles - 1);
+      const int lim = tile_ok ? rq.kv_len - kt * C::BN : 0;  // key row r exists iff r < lim
+      const int tp = ((kt * C::BN) >> page_shift) - key_lo_page;
+      int32_t pid[NCHT];
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i)
-      dma16(chunk_src(v ? vbase : kbase, v ? vcol[i] : kcol[i], t, i), buf + (uint32_t)((i * C::WAVES + wave) * 1024));
+      for (int i = 0; i < NCHT; ++i) pid[i] = pg_lds[tp + pg_rel[i]];
+#pragma unroll
+      for (int i = 0; i < NCHT; ++i) {
+        const bool ok = krow[i] < lim && pid[i] >= 0;
+        const uint64_t off = (uint64_t)(uint32_t)(ok ? pid[i] : 0) * (uint64_t)page_bytes +
+                             (uint64_t)in_page[i] + (uint64_t)(v ? vcol[i] : kcol[i]);
+        dma16(ok ? base + off : zero16, buf + (uint32_t)((i * IW + iw) * 1024));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NCHT; ++i)
+        dma16(chunk_src(base, v ? vcol[i] : kcol[i], t, i), buf + (uint32_t)((i * IW + iw) * 1024));
+    }
   };
   u32x2 kreg[C::NCH], vreg[C::NCH];  // fp8 staging of one load group
   auto fp8_load = [&](int tk, int tv) {
@@ -333,10 +410,65 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
   };
   auto issue_group = [&](int t) {  // bf16: DMA of load group t
-    dma_tile(false, t + C::NBUF);
-    dma_tile(true, t + C::NBUF - 2);
+    dma_tile(false, t + KA);
+    dma_tile(true, t + 2);
   };
-  constexpr int kGroupLoads = 2 * C::NCH;
+  // Scalar pages. Load i of this wave in tile t covers key rows [key0, key0 + KPI) of one
+  // page; its page id is read from the LDS table one iteration ahead (a uniform read that
+  // queues behind the iteration's other LDS traffic) and moved to a scalar register.
+  auto page_slot = [&](int t, int i) {
+    const int kt = kt0 + min(max(t, 0), n_tiles - 1);
+    const int key0 = kt * C::BN + (i * IW + iw) * C::KPI;
+    return min((key0 >> page_shift) - key_lo_page, n_pages - 1);
+  };
+  int64_t ids[2][NCHT];  // page byte offsets of the next group's K and V loads (uniform values)
+  auto read_ids = [&](int g) {
+#pragma unroll
+    for (int i = 0; i < NCHT; ++i) {
+      ids[0][i] = pg_off[page_slot(g + KA, i)];
+      ids[1][i] = pg_off[page_slot(g + 2, i)];
+    }
+  };
+  // Descriptors of the next group's loads, prepared ahead so that firing a load is an M0
+  // write and the load itself.
+  struct LoadDesc {
+    i32x4 rsrc;
+    uint32_t lds;
+  };
+  constexpr int kLoads = 2 * NCHT;
+  LoadDesc nd[kLoads];
+  auto prep = [&](int g) {  // from ids (group g's page offsets)
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) {
+      const bool v = j >= NCHT;
+      const int i = v ? j - NCHT : j;
+      const int t = v ? g + 2 : g + KA;
+      const int64_t off_lds = ids[v ? 1 : 0][i];
+      const uint64_t base = reinterpret_cast<uint64_t>(v ? vbase : kbase);
+      const bool tile_ok = t >= 0 && t < n_tiles;
+      const int key0 = (kt0 + min(max(t, 0), n_tiles - 1)) * C::BN + (i * IW + iw) * C::KPI;
+      const int64_t off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_lds)) |
+                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_lds >> 32)) << 32));
+      const int rows = min(max(rq.kv_len - key0, 0), C::KPI);
+      const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane(
+          (int)((tile_ok && off >= 0) ? (uint32_t)rows * (uint32_t)token_bytes : 0u));
+      const uint64_t addr = base + (uint64_t)off + (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
+      nd[j].rsrc = buffer_rsrc(addr, bytes);
+      nd[j].lds = lds0 + (uint32_t)(((v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES + (i * IW + iw) * 1024);
+    }
+  };
+  auto fire = [&](int j) { dma16_buf(j < NCHT ? voff_k[j] : voff_v[j - NCHT], nd[j].rsrc, nd[j].lds); };
+  auto issue_group_scalar = [&](int t) {  // ids hold group t's; then read group t+1's
+    prep(t);
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) fire(j);
+    read_ids(t + 1);
+  };
+  auto issue = [&](int t) {  // bf16: load group t
+    if constexpr (MODE == kPagesScalar) issue_group_scalar(t);
+    else issue_group(t);
+  };
+  constexpr int kGroupLoads = kLoads;
 
   // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
@@ -357,15 +489,23 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[kb][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // every s[kb][nb] accumulates head_dim chunks dc = 0, 1, ... in that order
+    // step st = (dc, kb) with dc outer: every s[kb][nb] accumulates head_dim chunks
+    // dc = 0, 1, ... in that order; each step's K operand is read kAhead steps ahead
+    constexpr int kS = C::DC * C::KB;
+    auto read_k = [&](int st) {
+      const int dc = st / C::KB, kb = st % C::KB;
+      return *reinterpret_cast<const bf16x8*>(k_lds + chunk_off<C::ROW_BYTES>(kb * 16 + li, dc * 4 + lg));
+    };
+    bf16x8 ka[kAhead + 1];
 #pragma unroll
-    for (int dc = 0; dc < C::DC; ++dc) {
+    for (int st = 0; st < kAhead; ++st) ka[st] = read_k(st);
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(k_lds + chunk_off<C::ROW_BYTES>(kb * 16 + li, dc * 4 + lg));
+    for (int st = 0; st < kS; ++st) {
+      if (st + kAhead < kS) ka[(st + kAhead) % (kAhead + 1)] = read_k(st + kAhead);
+      const int dc = st / C::KB, kb = st % C::KB;
 #pragma unroll
-        for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma16(ka, qreg[nb][dc], s[kb][nb]);
-      }
+      for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma16(ka[st % (kAhead + 1)], qreg[nb][dc], s[kb][nb]);
+      if constexpr (kPP) __builtin_amdgcn_sched_barrier(0);  // keep this order: reads kAhead steps ahead
     }
   };
 
@@ -433,64 +573,39 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
     return __any(moved);
   };
-  // O = alpha O (alpha = 1 exactly for the rows that kept their reference)
-  auto rescale = [&](const float (&alpha)[NB]) {
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb)
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha[nb];
-  };
 
   // O^T += V^T P^T for tile t. V^T comes transposed from the natural layout: lane (lg, r) of
   // read h points at key 32kc + 16h + 4lg + r/4, head_dim 16db + 4(r%4), and receives
   // V[32kc + 16h + 4lg + j][16db + li] for j = 0..3 -- the A operand's k = 8lg + 4h + j.
-  auto pv_acc = [&](const bf16x8 (&pb)[C::KC][NB], int t) {
+  auto no_hook = [](int) {};
+  auto pv_acc = [&](const bf16x8 (&pb)[C::KC][NB], int t, auto&& hook) {
     const unsigned char* v_lds = smem + (C::NBUF + (t & (C::NBUF - 1))) * C::TILE_BYTES;
-    // every acc[db][nb] accumulates key chunks kc = 0, 1, ... in that order
+    // step st = (kc, db) with kc outer: every acc[db][nb] accumulates key chunks kc = 0, 1,
+    // ... in that order; each step's V^T operand is read kAhead steps ahead
+    constexpr int kS = C::KC * C::DB;
+    auto read_v = [&](int st) {
+      const int kc = st / C::DB, db = st % C::DB;
+      s16x4 hv[2];
 #pragma unroll
-    for (int kc = 0; kc < C::KC; ++kc) {
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db) {
-        s16x4 hv[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
-          const int e = db * 16 + 4 * (li & 3);
-          const unsigned char* addr = v_lds + chunk_off_v<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
-          hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
-        }
-        const s16x8 v8 = __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7);
-        const bf16x8 va = __builtin_bit_cast(bf16x8, v8);
-#pragma unroll
-        for (int nb = 0; nb < NB; ++nb) acc[db][nb] = mfma16(va, pb[kc][nb], acc[db][nb]);
+      for (int h = 0; h < 2; ++h) {
+        const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
+        const int e = db * 16 + 4 * (li & 3);
+        const unsigned char* addr = v_lds + chunk_off_v<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
+        hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
       }
-    }
-  };
-
-  // Instruction order inside the two straight-line blocks of an iteration (the scheduler's
-  // groups: 0x008 MFMA, 0x402 vector ALU incl. transcendental, 0x100 LDS read). PV(t-1) with
-  // softmax(t): each step's V^T reads go two steps ahead of their MFMAs and the softmax
-  // arithmetic fills the gaps between MFMAs. QK^T(t+1): K reads two steps ahead.
-  constexpr int kSteps = C::DB * C::KC;  // PV steps: 2 V^T reads, NB MFMAs each
-  static_assert(kSteps == C::DC * C::KB, "QK^T has as many steps (1 K read, NB MFMAs)");
-  auto sched_pv_softmax = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+      return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
+    };
+    bf16x8 va[kAhead + 1];
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
+    for (int st = 0; st < kAhead; ++st) va[st] = read_v(st);
 #pragma unroll
-      for (int m = 0; m < NB; ++m) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
-        if (m == 0 && st + 2 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-      }
-    }
-  };
-  auto sched_qk = [&]() {
-    __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    for (int st = 0; st < kS; ++st) {
+      if (st + kAhead < kS) va[(st + kAhead) % (kAhead + 1)] = read_v(st + kAhead);
+      const int kc = st / C::DB, db = st % C::DB;
 #pragma unroll
-    for (int st = 0; st < kSteps; ++st) {
-      if (st + 2 < kSteps) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x008, NB, 0);
+      for (int nb = 0; nb < NB; ++nb) acc[db][nb] = mfma16(va[st % (kAhead + 1)], pb[kc][nb], acc[db][nb]);
+      hook(st);  // work to overlap with this step's MFMAs
+      if constexpr (kPP) __builtin_amdgcn_sched_barrier(0);  // keep this order: reads kAhead steps ahead
     }
   };
 
@@ -502,54 +617,129 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   // O = alpha(t) O, then O += PV(t). QK^T of the tile past the item reads a zero-filled
   // buffer and is discarded; PV(-1) adds V(-1) P(-1) = 0 * 0 (both zero-filled).
   f32x4 s[C::KB][NB];
-  bf16x8 p0[C::KC][NB], p1[C::KC][NB];
+  // P^T of the previous tile until PV has issued its MFMAs, then of the current one (the
+  // softmax writes it after PV's last read in program order)
+  bf16x8 pb[C::KC][NB];
 #pragma unroll
   for (int kc = 0; kc < C::KC; ++kc)
 #pragma unroll
-    for (int nb = 0; nb < NB; ++nb) p0[kc][nb] = p1[kc][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+    for (int nb = 0; nb < NB; ++nb) pb[kc][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-  if constexpr (FP8) {
-#pragma unroll
-    for (int t = -C::NBUF; t < -1; ++t) {
-      fp8_load(t + C::NBUF, t + C::NBUF - 2);
-      fp8_store(t + C::NBUF, t + C::NBUF - 2);
-    }
-    fp8_load(C::NBUF - 1, C::NBUF - 3);  // group -1, stored in iteration 0
-  } else {
-#pragma unroll
-    for (int t = -C::NBUF; t < 0; ++t) issue_group(t);
-    wait_vmcnt<2 * kGroupLoads>();  // groups -4 and -3 landed: K(0), K(1), V(-1)
-  }
-  __syncthreads();
-  if (has_rows) qk(s, 0);
-  // load group 0 overwrites K(0): every wave's QK^T(0) must be done with it first
-  if constexpr (!FP8) __syncthreads();
-
-  // p_prv/p_cur alternate between the two register sets (no copies)
-  auto iteration = [&](int t, bf16x8 (&p_prv)[C::KC][NB], bf16x8 (&p_cur)[C::KC][NB]) {
+  if constexpr (!kPP) {
     if constexpr (FP8) {
-      fp8_store(t + C::NBUF - 1, t + C::NBUF - 3);  // group t-1
-      fp8_load(t + C::NBUF, t + C::NBUF - 2);       // group t
+#pragma unroll
+      for (int t = -C::NBUF; t < -1; ++t) {
+        fp8_load(t + C::NBUF, t + C::NBUF - 2);
+        fp8_store(t + C::NBUF, t + C::NBUF - 2);
+      }
+      fp8_load(C::NBUF - 1, C::NBUF - 3);  // group -1, stored in iteration 0
     } else {
-      issue_group(t);
+      if (issuer) {
+        if constexpr (MODE == kPagesScalar) {
+          read_ids(-C::NBUF);
+#pragma unroll
+          for (int t = -C::NBUF; t < 0; ++t) issue_group_scalar(t);
+        } else {
+#pragma unroll
+          for (int t = -C::NBUF; t < 0; ++t) issue_group(t);
+        }
+      }
+      wait_vmcnt<2 * kGroupLoads>();  // groups -4 and -3 landed: K(0), K(1), V(-1)
     }
-    if (has_rows) {
-      if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
-      float alpha[NB];
-      pv_acc(p_prv, t - 1);
-      softmax(s, p_cur, alpha);
-      qk(s, t + 1);
-    }
-    if constexpr (!FP8) wait_vmcnt<2 * kGroupLoads>();  // group t-2 landed
     __syncthreads();
-  };
-  for (int t = 0; t < n_tiles; t += 2) {
-    iteration(t, p0, p1);
-    if (t + 1 < n_tiles) iteration(t + 1, p1, p0);
-  }
-  if (has_rows) {
-    if (n_tiles & 1) pv_acc(p1, n_tiles - 1);
-    else pv_acc(p0, n_tiles - 1);
+    if (has_rows) qk(s, 0);
+    // load group 0 overwrites K(0): every wave's QK^T(0) must be done with it first
+    if constexpr (!FP8) __syncthreads();
+
+    auto iteration = [&](int t) {
+      if constexpr (FP8) {
+        fp8_store(t + C::NBUF - 1, t + C::NBUF - 3);  // group t-1
+        fp8_load(t + C::NBUF, t + C::NBUF - 2);       // group t
+      } else if constexpr (MODE == kPagesScalar) {
+        if (issuer) issue_group_scalar(t);
+      } else {
+        if (issuer) issue_group(t);
+      }
+      if (has_rows) {
+        if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
+        float alpha[NB];
+        pv_acc(pb, t - 1, no_hook);
+        softmax(s, pb, alpha);
+        qk(s, t + 1);
+      }
+      if constexpr (!FP8) wait_vmcnt<2 * kGroupLoads>();  // group t-2 landed
+      __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; ++t) iteration(t);
+    if (has_rows) pv_acc(pb, n_tiles - 1, no_hook);
+  } else {
+    // Two groups: waves 0-3 lead, waves 4-7 (which share the SIMDs with them pairwise) run
+    // one phase behind. Per tile t two phases, each closed by a barrier:
+    //   B(t)  mask + softmax(t)                                   -- vector ALU
+    //   A(t)  PV(t) firing own part of load group t+1, QK^T(t+1)  -- matrix cores
+    // so that one wave of a SIMD computes a softmax while the other runs MFMAs. Load group t
+    // brings K(t+3) and V(t+2); A(t) reads K(t+1) and V(t), both from group t-2. Every wave
+    // waits for its own part of a group before the barrier that opens the leading group's
+    // A phase reading it: the leading waves at the end of B(t) for group t-2, the trailing
+    // waves (whose B(t) falls in the leading group's A(t)) at the end of their A(t) for
+    // group t-1. Group t overwrites K(t-1) and V(t-2), last read by the trailing group's
+    // A(t-2), one phase before any wave issues group t (in its A(t-1)). Groups -3..0 are
+    // issued up front. Per row the sequence is the plain one: O = alpha(t) O, then
+    // O += PV(t).
+    const bool leading = wave < C::WAVES / 2;
+    if constexpr (MODE == kPagesScalar) {
+      read_ids(-3);
+#pragma unroll
+      for (int g = -3; g <= 0; ++g) {
+        prep(g);
+#pragma unroll
+        for (int j = 0; j < kLoads; ++j) fire(j);
+        read_ids(g + 1);
+      }
+    } else {
+#pragma unroll
+      for (int g = -3; g <= 0; ++g) issue(g);
+    }
+    wait_vmcnt<3 * kGroupLoads>();  // group -3 landed: K(0), V(-1)
+    __syncthreads();
+    if (has_rows) qk(s, 0);
+    if (!leading) {
+      wait_vmcnt<2 * kGroupLoads>();  // group -2 (K(1), V(0)) before the leading group's A(0)
+      __syncthreads();
+    }
+    // group g's loads are prepared in B(g-1) and fired between the PV steps of A(g-1)
+    constexpr int kEvery = (C::KC * C::DB) / kLoads;
+    static_assert(kEvery >= 1, "one load per PV step at most");
+    for (int t = 0; t < n_tiles; ++t) {
+      if (has_rows) {
+        if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
+        float alpha[NB];
+        softmax(s, pb, alpha);
+      }
+      if constexpr (MODE == kPagesScalar) prep(t + 1);
+      // A(t) reads group t-2; the leading group's A(t) starts at the next barrier, the
+      // trailing group's one phase later (its wait for group t-1 follows its A(t))
+      if (leading) wait_vmcnt<2 * kGroupLoads>();
+      __syncthreads();
+      if constexpr (MODE == kPagesScalar) {
+        if (has_rows) {
+          pv_acc(pb, t, [&](int st) {
+            if (st % kEvery == 0 && st / kEvery < kLoads) fire(st / kEvery);
+          });
+        } else {
+#pragma unroll
+          for (int j = 0; j < kLoads; ++j) fire(j);
+        }
+        read_ids(t + 2);
+      } else {
+        issue(t + 1);
+        if (has_rows) pv_acc(pb, t, no_hook);
+      }
+      if (has_rows && t + 1 < n_tiles) qk(s, t + 1);
+      if (!leading) wait_vmcnt<2 * kGroupLoads>();  // group t-1, for the leading group's A(t+1)
+      __syncthreads();
+    }
+    if (leading) __syncthreads();
   }
   wait_vmcnt<0>();  // no load may outlive the workgroup (a DMA load would land in LDS)
 
@@ -585,31 +775,40 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   }
 }
 
-template <int D, bool FP8, int NB, bool P2>
+template <int D, bool FP8, int NB, int MODE>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   using C = Geo<D, NB>;
-  // page-id table: the item's pages plus one tile's worth of slack for the last tile's
-  // lookups past kv_len (their chunks read the zero chunk)
-  const size_t lds = (size_t)C::LDS_BYTES + ((size_t)a.page_slots + C::BN) * 4;
+  // page table: the item's pages plus one tile's worth of slack for the last tile's lookups
+  // past kv_len (their chunks read the zero chunk); byte offsets (8 bytes) in scalar mode,
+  // page ids (4 bytes) otherwise
+  constexpr size_t kEntry = MODE == kPagesScalar ? 8 : 4;
+  const size_t lds = (size_t)C::LDS_BYTES + ((size_t)a.page_slots + C::BN) * kEntry;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, P2>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
   }
   dim3 grid((unsigned)(a.num_items * a.num_kv_heads));
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, P2>), grid, dim3(C::THREADS), lds, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
 template <int D, int NB>
 hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   const int P = a.page_size;
-  const bool p2 = (P & (P - 1)) == 0 && P <= block_n_for(D);
-  if (fp8) return p2 ? launch_one<D, true, NB, true>(a, stream) : launch_one<D, true, NB, false>(a, stream);
-  return p2 ? launch_one<D, false, NB, true>(a, stream) : launch_one<D, false, NB, false>(a, stream);
+  const bool pow2 = (P & (P - 1)) == 0;
+  if (fp8) {
+    return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, kPagesPow2>(a, stream)
+                                       : launch_one<D, true, NB, kPagesGeneral>(a, stream);
+  }
+  // The narrow kernel's issuing waves compute nothing else: per-lane (vector) addresses
+  // suit them. The wide kernel's waves are busy with the softmax: scalar descriptors.
+  if (NB > 1 && pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
+  return pow2 && P <= block_n_for(D) ? launch_one<D, false, NB, kPagesPow2>(a, stream)
+                                     : launch_one<D, false, NB, kPagesGeneral>(a, stream);
 }
 
 template <int D>

@@ -10,7 +10,8 @@ HEADER_WORDS = 16
 @dataclass
 class ParsedPlan:
     requests: np.ndarray  # [B, 4]: q_start, qo_len, page_start, kv_len
-    items: np.ndarray     # [N, 8]: request, row_start, split, tile_splits, kv_tile_begin, kv_tile_end, slot_base, pad
+    items: np.ndarray     # [N, 16]: request, row_start, split, tile_splits, kv_tile_begin, kv_tile_end,
+                          # slot_base, pad, then the request's q_start, qo_len, page_start, kv_len, pad x4
     merges: np.ndarray    # [M, 4]: request, row_start, tile_splits, slot_base
 
 
@@ -19,6 +20,6 @@ def parse(words: np.ndarray) -> ParsedPlan:
     assert (int(w[0]) & 0xFFFFFFFF) == MAGIC
     nreq, nitems, nmerge, roff, ioff, moff = (int(x) for x in w[1:7])
     req = w[roff:roff + 4 * nreq].reshape(nreq, 4)
-    items = w[ioff:ioff + 8 * nitems].reshape(nitems, 8)
+    items = w[ioff:ioff + 16 * nitems].reshape(nitems, 16)
     merges = w[moff:moff + 4 * nmerge].reshape(nmerge, 4)
     return ParsedPlan(req, items, merges)

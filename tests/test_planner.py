@@ -73,8 +73,10 @@ def _coverage(parsed, g, bm):
     """Map (request, packed row, split) -> KV tile range visited; check exactly-once."""
     seen = {}
     for it in parsed.items:
-        r, rs, s, S, kb, ke, slot, _ = (int(x) for x in it)
+        r, rs, s, S, kb, ke, slot = (int(x) for x in it[:7])
         q_start, qo_len, page_start, kv_len = parsed.requests[r]
+        # the item carries a copy of its request's descriptor
+        assert [int(x) for x in it[8:12]] == [int(q_start), int(qo_len), int(page_start), int(kv_len)]
         rows = min(bm, qo_len * g - rs)
         for lr in range(rows):
             key = (r, rs + lr, s)
@@ -141,7 +143,7 @@ def test_workspace_closed_form_single_pass(dpp):
             ntile += 1
             if S > 1:
                 slots += S * 8 * bm
-    words = 16 + 4 * len(specs) + 8 * len(parsed.items) + 4 * len(parsed.merges)
+    words = 16 + 4 * len(specs) + 16 * len(parsed.items) + 4 * len(parsed.merges)
     hdr = _align(words * 4)
     assert p.info.header_bytes == hdr
     assert p.info.max_partial_slots == slots
