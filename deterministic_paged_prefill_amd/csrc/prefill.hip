@@ -36,6 +36,7 @@
 
 #include <climits>
 #include <cstdint>
+#include <type_traits>
 
 #include "dpp_internal.h"
 #include "kernels.h"
@@ -56,8 +57,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 constexpr float kLn2 = 0.693147180559945309417f;
 // Rebase threshold of the online softmax's reference max, in log2 units (P_j <= 2^8).
 constexpr float kRebase = 8.0f;
-// LDS operand reads of QK^T and PV run this many MFMA steps ahead of their use.
-constexpr int kAhead = 3;
+// LDS operand reads of QK^T and PV run this many MFMA steps ahead of their use: a step is
+// NB MFMAs, so a wave with one 16-row block reads further ahead.
+template <int NB>
+constexpr int ahead_for() { return NB == 1 ? 7 : 3; }
 
 template <int D, int NB>
 struct Geo {
@@ -77,6 +80,9 @@ struct Geo {
   static constexpr int NCH = BN * CH / THREADS;    // 16-byte chunks per thread per tensor per tile
   static constexpr int KPI = 64 * 16 / ROW_BYTES;  // key rows one wave-wide DMA load covers
   static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
+  // narrow bf16 kernel: P^T and alpha of two tiles, then l and m, passed between two waves
+  static constexpr int XSLOT = 64 * KC * 16 + 64 * 4;
+  static constexpr int XBYTES = 2 * XSLOT + 2 * 64 * 4;
   static_assert(NCH * THREADS == BN * CH, "the threads cover a tile");
   static_assert(NCH * 64 * WAVES * 16 == TILE_BYTES, "one DMA load per wave moves 1 KiB");
   static_assert(RPW * WAVES >= kNarrowRows && RPW * WAVES <= PLAN_BM, "tile rows fit the waves");
@@ -198,8 +204,13 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   using C = Geo<D, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // page table of the item: page ids (-1 = bad id), or in scalar mode the pages' byte offsets
-  int32_t* pg_lds = reinterpret_cast<int32_t*>(smem + C::LDS_BYTES);
-  int64_t* pg_off = reinterpret_cast<int64_t*>(smem + C::LDS_BYTES);
+  // Narrow bf16 kernel with eight waves: wave 0 computes scores and softmax, wave 4 (on the
+  // same SIMD) the output, and waves 2, 3, 6, 7 issue the DMA loads.
+  constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
+  unsigned char* xb = smem + C::LDS_BYTES;  // exchange buffer (kSpec)
+  unsigned char* pt = xb + (kSpec ? C::XBYTES : 0);
+  int32_t* pg_lds = reinterpret_cast<int32_t*>(pt);
+  int64_t* pg_off = reinterpret_cast<int64_t*>(pt);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -224,13 +235,16 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int lg = lane >> 4;                // 16-lane group: 8-wide k slice in, 4 output rows out
   const int li = lane & 15;                // column (query row) within a 16-row block
   const int split_key0 = it.split * kSplitTokens;
-  const bool has_rows = wave * C::RPW < tile_rows;  // wave-uniform
+  const int row_wave = kSpec ? 0 : wave;  // whose 16-row blocks this wave works on
+  const bool has_rows = row_wave * C::RPW < tile_rows;  // wave-uniform
+  const bool s_rows = has_rows && (!kSpec || wave == 0);  // scores and softmax
+  const bool o_rows = has_rows && (!kSpec || wave == 4);  // output
 
   // Rows of this lane: tile-local packed row lr = RPW*wave + 16*nb + li.
   int p_row[NB];  // position of the row (INT_MAX past the tile: no key is masked)
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int lr = wave * C::RPW + nb * 16 + li;
+    const int lr = row_wave * C::RPW + nb * 16 + li;
     p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
   }
   const int p_min = ctx + it.row_start / g;
@@ -257,8 +271,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   bf16x8 qreg[NB][C::DC];
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int lr = wave * C::RPW + nb * 16 + li;
-    const bool valid = lr < tile_rows;
+    const int lr = row_wave * C::RPW + nb * 16 + li;
+    const bool valid = lr < tile_rows && s_rows;
     const int R = it.row_start + lr;
     const int token = R / g;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
@@ -291,12 +305,10 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   static_assert(!(FP8 && MODE == kPagesScalar), "fp8 stages through registers");
   // Two-group schedule (see below): bf16 wide tiles with two waves per SIMD.
   constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
-  // The narrow instantiation's computing wave is wave 0 alone: with eight waves, waves 4-7
-  // issue all of its DMA loads. Otherwise every wave issues its share.
-  constexpr int kIssuer0 = (!FP8 && NB == 1 && C::WAVES == 8) ? 4 : 0;
-  constexpr int IW = C::WAVES - kIssuer0;                 // waves that issue DMA loads
-  const int iw = wave - kIssuer0;                         // this wave's index among them
-  const bool issuer = iw >= 0;
+  // Waves that issue DMA loads: 2, 3, 6, 7 in the narrow bf16 kernel, otherwise all.
+  constexpr int IW = kSpec ? 4 : C::WAVES;
+  const int iw = kSpec ? ((wave & 1) | ((wave >> 2) << 1)) : wave;  // index among the issuers
+  const bool issuer = !kSpec || (wave & 2) != 0;
   constexpr int NL = C::TILE_BYTES / (IW * 1024);         // their loads per tensor per tile
   constexpr int NCHT = FP8 ? C::NCH : NL;                 // chunks per thread per tensor per tile
   constexpr int KA = kPP ? 3 : C::NBUF;                   // load group t brings K(t + KA), V(t + 2)
@@ -482,6 +494,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     for (int db = 0; db < C::DB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  constexpr int kAhead = ahead_for<NB>();
+  constexpr bool kPin = kPP || NB == 1;  // pin the read-ahead order (the scheduler undoes it)
   // S^T = K Q^T for tile t
   auto qk = [&](f32x4 (&s)[C::KB][NB], int t) {
     const unsigned char* k_lds = smem + (t & (C::NBUF - 1)) * C::TILE_BYTES;
@@ -505,7 +519,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       const int dc = st / C::KB, kb = st % C::KB;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) s[kb][nb] = mfma16(ka[st % (kAhead + 1)], qreg[nb][dc], s[kb][nb]);
-      if constexpr (kPP) __builtin_amdgcn_sched_barrier(0);  // keep this order: reads kAhead steps ahead
+      if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);  // keep this order: reads kAhead steps ahead
     }
   };
 
@@ -524,7 +538,9 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 
   // online softmax of one tile: P^T into pb, alpha per row block; returns whether some row
   // of the wave moved its reference (then O must be rescaled by alpha, see rescale)
-  auto softmax = [&](f32x4 (&s)[C::KB][NB], bf16x8 (&pb)[C::KC][NB], float (&alpha)[NB]) -> bool {
+  auto softmax = [&](f32x4 (&s)[C::KB][NB], bf16x8 (&pb)[C::KC][NB], float (&alpha)[NB],
+                     auto rescale_tag) -> bool {
+    constexpr bool kRescale = decltype(rescale_tag)::value;  // O lives in this wave
     bool moved = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
@@ -557,9 +573,11 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         for (int i = 0; i < h; ++i) ts[i] = ts[2 * i] + ts[2 * i + 1];
       const float rs = row_sum4(ts[0]);
       l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha[nb], rs);
-      if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
+      if constexpr (kRescale) {
+        if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha[nb];
+          for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha[nb];
+        }
       }
       // P^T as the PV B operand: k = 8lg + i is key 32kc + 16(i/4) + 4lg + i%4
 #pragma unroll
@@ -605,7 +623,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[db][nb] = mfma16(va[st % (kAhead + 1)], pb[kc][nb], acc[db][nb]);
       hook(st);  // work to overlap with this step's MFMAs
-      if constexpr (kPP) __builtin_amdgcn_sched_barrier(0);  // keep this order: reads kAhead steps ahead
+      if constexpr (kPin) __builtin_amdgcn_sched_barrier(0);  // keep this order: reads kAhead steps ahead
     }
   };
 
@@ -625,7 +643,79 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) pb[kc][nb] = __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
 
-  if constexpr (!kPP) {
+  if constexpr (kSpec) {
+    // Narrow bf16 kernel: same load schedule as the plain loop below (group t brings K(t+4)
+    // and V(t+2), issued in iteration t, landed before the barrier ending iteration t+2).
+    // Iteration t: wave 0 masks S(t), runs softmax(t) into P(t) and alpha(t), hands them to
+    // wave 4 through LDS slot t&1 and computes QK^T(t+1) into its other score registers;
+    // wave 4 takes P(t-1), alpha(t-1) from slot (t-1)&1, rescales O by alpha(t-1) (alpha = 1
+    // exactly for the rows that kept their reference) and adds PV(t-1). The two waves share
+    // a SIMD, so the softmax arithmetic of one runs beside the MFMAs of the other. Per row
+    // the sequence is the plain one: O = alpha(t) O, then O += PV(t). A slot is rewritten
+    // two iterations after it was filled, one barrier after wave 4 read it.
+    if (issuer) {
+      if constexpr (MODE == kPagesScalar) {
+        read_ids(-C::NBUF);
+#pragma unroll
+        for (int t = -C::NBUF; t < 0; ++t) issue_group_scalar(t);
+      } else {
+#pragma unroll
+        for (int t = -C::NBUF; t < 0; ++t) issue_group(t);
+      }
+      wait_vmcnt<2 * kGroupLoads>();  // groups -4 and -3 landed: K(0), K(1), V(-1)
+    }
+    __syncthreads();
+    f32x4 s1[C::KB][NB];
+    if (s_rows) qk(s, 0);
+    __syncthreads();  // load group 0 overwrites K(0)
+    auto put_p = [&](int t, const float (&al)[NB]) {
+      unsigned char* slot = xb + (t & 1) * C::XSLOT;
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) *reinterpret_cast<bf16x8*>(slot + (kc * 64 + lane) * 16) = pb[kc][0];
+      *reinterpret_cast<float*>(slot + 64 * C::KC * 16 + lane * 4) = al[0];
+    };
+    auto take_p = [&](int t) {  // wave 4: P^T and alpha of tile t, then O = alpha O + PV(t)
+      const unsigned char* slot = xb + (t & 1) * C::XSLOT;
+#pragma unroll
+      for (int kc = 0; kc < C::KC; ++kc) pb[kc][0] = *reinterpret_cast<const bf16x8*>(slot + (kc * 64 + lane) * 16);
+      const float al = *reinterpret_cast<const float*>(slot + 64 * C::KC * 16 + lane * 4);
+#pragma unroll
+      for (int db = 0; db < C::DB; ++db) acc[db][0] *= al;
+      pv_acc(pb, t, no_hook);
+    };
+    auto spec_iter = [&](int t, f32x4 (&sc)[C::KB][NB], f32x4 (&sn)[C::KB][NB]) {
+      if (issuer) {
+        if constexpr (MODE == kPagesScalar) issue_group_scalar(t);
+        else issue_group(t);
+      }
+      if (s_rows) {
+        if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(sc, t);
+        float alpha[NB];
+        softmax(sc, pb, alpha, std::false_type{});
+        put_p(t, alpha);
+        if (t + 1 < n_tiles) qk(sn, t + 1);
+      }
+      if (o_rows && t >= 1) take_p(t - 1);
+      if (issuer) wait_vmcnt<2 * kGroupLoads>();  // group t-2 landed
+      __syncthreads();
+    };
+    for (int t = 0; t < n_tiles; t += 2) {
+      spec_iter(t, s, s1);
+      if (t + 1 < n_tiles) spec_iter(t + 1, s1, s);
+    }
+    if (o_rows) take_p(n_tiles - 1);
+    // l and m of the rows to wave 4, which writes the outputs
+    float* xl = reinterpret_cast<float*>(xb + 2 * C::XSLOT);
+    if (s_rows) {
+      xl[lane] = l_sum[0];
+      xl[64 + lane] = m_sc[0];
+    }
+    __syncthreads();
+    if (o_rows) {
+      l_sum[0] = xl[lane];
+      m_sc[0] = xl[64 + lane];
+    }
+  } else if constexpr (!kPP) {
     if constexpr (FP8) {
 #pragma unroll
       for (int t = -C::NBUF; t < -1; ++t) {
@@ -664,7 +754,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
         float alpha[NB];
         pv_acc(pb, t - 1, no_hook);
-        softmax(s, pb, alpha);
+        softmax(s, pb, alpha, std::true_type{});
         qk(s, t + 1);
       }
       if constexpr (!FP8) wait_vmcnt<2 * kGroupLoads>();  // group t-2 landed
@@ -714,7 +804,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       if (has_rows) {
         if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
         float alpha[NB];
-        softmax(s, pb, alpha);
+        softmax(s, pb, alpha, std::true_type{});
       }
       if constexpr (MODE == kPagesScalar) prep(t + 1);
       // A(t) reads group t-2; the leading group's A(t) starts at the next barrier, the
@@ -744,10 +834,10 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   wait_vmcnt<0>();  // no load may outlive the workgroup (a DMA load would land in LDS)
 
   // ---- epilogue: lane holds O^T[d = 16db + 4lg + j][row 16nb + li]
-  if (!has_rows) return;
+  if (!o_rows) return;
 #pragma unroll
   for (int nb = 0; nb < NB; ++nb) {
-    const int lr = wave * C::RPW + nb * 16 + li;
+    const int lr = row_wave * C::RPW + nb * 16 + li;
     const int p = p_row[nb];
     if (lr >= tile_rows || p < split_key0) continue;  // not a row of this split
     const int R = it.row_start + lr;
@@ -782,7 +872,8 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   // past kv_len (their chunks read the zero chunk); byte offsets (8 bytes) in scalar mode,
   // page ids (4 bytes) otherwise
   constexpr size_t kEntry = MODE == kPagesScalar ? 8 : 4;
-  const size_t lds = (size_t)C::LDS_BYTES + ((size_t)a.page_slots + C::BN) * kEntry;
+  constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
+  const size_t lds = (size_t)C::LDS_BYTES + (kSpec ? C::XBYTES : 0) + ((size_t)a.page_slots + C::BN) * kEntry;
   if (lds > 160 * 1024) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
