@@ -139,8 +139,9 @@ def traffic_from_profile(launch_bytes: float):
         return None
     if prof.get("kernel_source_sha256_16") != kernel_hash():
         return None
-    scale = prof.get("copy_calibration_factor", 1.0)
-    return (prof["fetch_kib_per_dispatch"] + prof["write_kib_per_dispatch"]) * 1024.0 * scale
+    # each counter scaled by the bytes a plain device copy of known size moves per KiB it reads
+    return (prof["fetch_kib_per_dispatch"] * prof["fetch_bytes_per_kib"] +
+            prof["write_kib_per_dispatch"] * prof["write_bytes_per_kib"])
 
 
 def cpu_baseline(work, batch, budget_s: float):
