@@ -20,10 +20,9 @@ namespace dpp {
 
 // Tile geometry: constants of head_dim, never of the batch.
 // A packed query row is (token, q head within the kv head's group); row R of a request covers
-// token R / group and q head kv_head * group + R % group. A workgroup is 4 waves, one per
-// SIMD, each owning rows_per_wave packed rows as 16-row MFMA column blocks: 64 rows at
-// head_dim <= 128 (256-row tiles), 32 at head_dim 256 (128-row tiles), sized to the 512
-// registers a wave has when it is alone on its SIMD.
+// token R / group and q head kv_head * group + R % group. Every wave owns 32 packed rows as
+// two 16-row MFMA column blocks; a workgroup is 8 waves (two per SIMD, 256-row tiles) at
+// head_dim <= 128 and 4 waves (one per SIMD, 128-row tiles) at head_dim 256.
 DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim <= 128 ? 32 : 32; }
 DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 128 ? 8 : 4; }
 DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) {
@@ -36,6 +35,17 @@ constexpr int kNarrowRows = 16;
 // Keys per KV tile. Tiles start at absolute key positions 0, BN, 2BN, ...
 DPP_HOST_DEVICE constexpr int block_n_for(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 constexpr int kMaxBlockM = 256;
+// LDS of a workgroup: a ring of four K and four V tiles (bf16), then page-id tables (4 bytes
+// an entry; two in a persistent launch, one per unit in flight), within the 160 KiB of a CU.
+DPP_HOST_DEVICE constexpr int ring_bytes_for(int head_dim) { return 2 * 4 * block_n_for(head_dim) * head_dim * 2; }
+constexpr int kLdsLimit = 160 * 1024;
+// Output staging of the two-group schedule: 2 KiB for each wave of a group.
+constexpr int kOutStageBytes = 4 * 2048;
+// Bytes of one page-id table for units spanning up to page_slots pages: the ids arrive by
+// whole 64-entry DMA loads, and the last KV tile may look up to one tile of keys past kv_len.
+DPP_HOST_DEVICE constexpr int64_t page_table_bytes(int64_t page_slots, int head_dim) {
+  return ((page_slots + 63) / 64 * 64 + block_n_for(head_dim)) * 4;
+}
 constexpr int kMergeThreads = 256;
 
 // Fixed KV split length (the model-serving-minefield issue #73 correction comment,
@@ -49,6 +59,17 @@ DPP_HOST_DEVICE inline int xcd_chunked(int b, int n) {
   const int q = n / kXcds, r = n % kXcds;
   const int x = b % kXcds;
   return x * q + (x < r ? x : r) + b / kXcds;
+}
+
+// Persistent launches. A wide bf16 launch at head_dim <= 128 (eight waves) runs as this many
+// workgroups -- one per compute unit of an MI355X; the LDS ring leaves room for one workgroup
+// per CU -- each working through a chain of units (item, kv head) fixed by the planner. The
+// chain a unit lands in decides when it runs, never its arithmetic.
+constexpr int kPersistentBlocks = 256;
+// Planner's cost estimate of a unit: its KV tiles plus this many tiles' worth of start-up.
+constexpr int kUnitOverheadTiles = 2;
+DPP_HOST_DEVICE constexpr bool chained_launch(int head_dim, bool fp8, bool narrow) {
+  return !fp8 && !narrow && waves_for(head_dim) == 8;
 }
 
 constexpr int kSplitTokens = 4096;
@@ -82,6 +103,19 @@ struct PrefillItem {
   RequestDesc req;       // the request's descriptor
   int32_t pad1[4];
 };
+// Unit record of a persistent launch: the item's record with four words reused. Workgroup b
+// of the launch starts at record b of its pass and follows `next` (an index into the pass's
+// records, -1 after its last unit).
+struct UnitRecord {
+  int32_t request, row_start, split, tile_splits, kv_tile_begin, kv_tile_end, slot_base;
+  int32_t next;
+  RequestDesc req;
+  int32_t kv_head;
+  int32_t block;         // workgroup that runs it
+  int32_t pass;
+  int32_t pad;
+};
+static_assert(sizeof(UnitRecord) == sizeof(PrefillItem), "unit record is an item record");
 static_assert(sizeof(PrefillItem) == 64, "item record is 16 words");
 constexpr int kItemWords = 16;
 
@@ -108,10 +142,13 @@ struct HeaderPreamble {
   int32_t item_offset;
   int32_t merge_offset;
   uint32_t plan_id;        // unique per plan; kernels refuse a header with another id
-  int32_t reserved[kHeaderWords - 8];  // zero; the gather reads its first 16 bytes as a zero chunk
+  int32_t zero_chunk[4];   // zero: the gather reads these 16 bytes in place of a missing chunk
+  int32_t unit_offset;     // word offset of the unit records (all passes), 0 if none
+  int32_t num_units;
+  int32_t reserved[2];     // zero
 };
 static_assert(sizeof(HeaderPreamble) == kHeaderWords * 4, "preamble size");
-static_assert(offsetof(HeaderPreamble, reserved) % 16 == 0, "zero chunk must be 16-byte aligned");
+static_assert(offsetof(HeaderPreamble, zero_chunk) % 16 == 0, "zero chunk must be 16-byte aligned");
 
 // ---- kernel launch arguments ----
 
@@ -128,13 +165,16 @@ struct PrefillArgs {
   int64_t num_pages;
   uint32_t plan_id;
   int32_t item_offset;      // word offset of the item records in the header
-  int32_t item_begin;       // first item of this pass
-  int32_t num_items;        // items in this pass
+  int32_t item_begin;       // first item of this launch
+  int32_t num_items;        // items in this launch
+  int32_t chain_offset;     // persistent launch: word offset of its unit records; -1: block b
+                            // runs unit xcd_chunked(b, num_items * num_kv_heads)
+  int32_t num_chains;       // persistent launch: its workgroups (one per chain)
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t group;
   int32_t page_size;
-  int32_t page_slots;       // entries of the per-item page-id table in LDS
+  int32_t page_slots;       // entries of one unit's page-id table in LDS
   float scale_log2;         // sm_scale * log2(e), rounded once to fp32
   float k_scale;
   float v_scale;

@@ -14,8 +14,14 @@
 //    split buffer crashing a server);
 //  * order: inside a pass, requests with the longest item first, a request's items kept
 //    together and longest first (load balance, and L2 reuse of the request's KV); a pass of
-//    tiles with at most kNarrowRows rows each runs on the narrow kernel. Order, passes, cap
-//    and kernel instantiation change when and where a row is computed, never its arithmetic.
+//    tiles with at most kNarrowRows rows each runs on the narrow kernel;
+//  * persistent chains: a wide bf16 pass at head_dim <= 128 runs as kPersistentBlocks
+//    workgroups, each over a chain of units (item, kv head). The units that the plain launch
+//    order would send to XCD x (a contiguous run, see xcd_chunked) are dealt longest first
+//    to the least loaded of the workgroups on XCD x (b % kXcds == x), each chain then
+//    rotated by the workgroup's rank on its XCD. Order, passes, cap,
+//    chains and kernel instantiation change when and where a row is computed, never its
+//    arithmetic.
 #include "plan.h"
 
 #include <algorithm>
@@ -50,6 +56,71 @@ struct TileInfo {
 };
 
 // Largest slot count n with align(n*D*4) + align(n*4) <= avail.
+// Persistent chains of one wide pass whose units are (item i, kv head h), unit w = h * n + i
+// for the n items at `items`: records placed so that workgroup b starts at record b.
+std::vector<UnitRecord> build_chains(const PrefillItem* items, int32_t n, int32_t num_kv_heads,
+                                     int32_t pass) {
+  const int64_t n_units = (int64_t)n * num_kv_heads;
+  const int32_t nb = (int32_t)std::min<int64_t>(n_units, kPersistentBlocks);
+  std::vector<UnitRecord> rec((size_t)n_units);
+  int32_t next_free = nb;
+  const int64_t q = n_units / kXcds, r = n_units % kXcds;
+  for (int x = 0; x < kXcds; ++x) {
+    const int64_t u0 = x * q + std::min<int64_t>(x, r), len = q + (x < r ? 1 : 0);
+    std::vector<int32_t> blocks;
+    for (int32_t b = x; b < nb; b += kXcds) blocks.push_back(b);
+    if (len == 0) continue;
+    std::vector<int64_t> order((size_t)len);
+    for (int64_t k = 0; k < len; ++k) order[(size_t)k] = u0 + k;
+    auto cost = [&](int64_t u) {
+      const PrefillItem& it = items[u % n];
+      return (int64_t)(it.kv_tile_end - it.kv_tile_begin) + kUnitOverheadTiles;
+    };
+    std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
+    std::vector<int64_t> load(blocks.size(), 0);
+    std::vector<std::vector<int64_t>> chain(blocks.size());
+    for (int64_t u : order) {
+      size_t k = 0;
+      for (size_t j = 1; j < blocks.size(); ++j)
+        if (load[j] < load[k]) k = j;
+      load[k] += cost(u);
+      chain[k].push_back(u);
+    }
+    // A workgroup's finish time is the sum over its chain, whatever the order; rotating the
+    // j-th workgroup's chain by j keeps neighbours from switching units (a burst of Q reads
+    // and O writes) at the same moments.
+    for (size_t k = 0; k < blocks.size(); ++k) {
+      std::vector<int64_t>& c = chain[k];
+      if (c.empty()) continue;
+      std::rotate(c.begin(), c.begin() + (std::ptrdiff_t)(k % c.size()), c.end());
+      const int32_t b = blocks[k];
+      int32_t prev_idx = -1;
+      for (size_t j = 0; j < c.size(); ++j) {
+        const int64_t u = c[j];
+        const int32_t idx = j == 0 ? b : next_free++;
+        if (prev_idx >= 0) rec[(size_t)prev_idx].next = idx;
+        prev_idx = idx;
+        const PrefillItem& it = items[u % n];
+        UnitRecord& ur = rec[(size_t)idx];
+        ur.request = it.request;
+        ur.row_start = it.row_start;
+        ur.split = it.split;
+        ur.tile_splits = it.tile_splits;
+        ur.kv_tile_begin = it.kv_tile_begin;
+        ur.kv_tile_end = it.kv_tile_end;
+        ur.slot_base = it.slot_base;
+        ur.next = -1;
+        ur.req = it.req;
+        ur.kv_head = (int32_t)(u / n);
+        ur.block = b;
+        ur.pass = pass;
+        ur.pad = 0;
+      }
+    }
+  }
+  return rec;
+}
+
 int64_t max_slots_for(size_t avail, int head_dim) {
   const size_t per_slot = (size_t)(head_dim + 1) * 4;
   int64_t n = (int64_t)(avail / per_slot);
@@ -137,19 +208,25 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     n_items += t.splits;
     n_merges += t.splits > 1 ? 1 : 0;
   }
-  const int64_t words = kHeaderWords + 4 * (int64_t)batch_size + kItemWords * n_items + 4 * n_merges;
-  if (n_items > std::numeric_limits<int32_t>::max() / 2 / c.num_kv_heads ||
-      words > std::numeric_limits<int32_t>::max() / 2)
+  if (n_items > std::numeric_limits<int32_t>::max() / 2 / c.num_kv_heads / kItemWords)
     return fail(DPP_ERR_UNSUPPORTED, "batch too large for one plan");
-  const size_t header_bytes = align_up((size_t)words * 4, 256);
+  // Unit records of persistent launches: at most one per (item, kv head).
+  const bool chain_kind = chained_launch(c.head_dim, c.kv_dtype == DPP_KV_FP8_E4M3, false);
+  const int64_t max_units = chain_kind ? n_items * c.num_kv_heads : 0;
+  const int64_t words_max = kHeaderWords + 4 * (int64_t)batch_size + kItemWords * (n_items + max_units) + 4 * n_merges;
+  if (words_max > std::numeric_limits<int32_t>::max() / 2)
+    return fail(DPP_ERR_UNSUPPORTED, "batch too large for one plan");
+  // The cap is checked against the largest header this plan can have (its unit records
+  // depend on the passes, which depend on the cap).
+  const size_t header_bytes_max = align_up((size_t)words_max * 4, 256);
 
   int64_t slot_limit = std::numeric_limits<int32_t>::max() / 2;
   if (workspace_cap > 0) {
-    if (workspace_cap < header_bytes)
+    if (workspace_cap < header_bytes_max)
       return fail(DPP_ERR_WORKSPACE, "workspace cap " + std::to_string(workspace_cap) +
                                          " B is below the work list's " +
-                                         std::to_string(header_bytes) + " B");
-    slot_limit = std::min<int64_t>(slot_limit, max_slots_for(workspace_cap - header_bytes, c.head_dim));
+                                         std::to_string(header_bytes_max) + " B");
+    slot_limit = std::min<int64_t>(slot_limit, max_slots_for(workspace_cap - header_bytes_max, c.head_dim));
   }
 
   // Passes: tiles in request order; a tile needing partials takes S_t * Hkv * block_m slots.
@@ -160,7 +237,7 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     if (need > slot_limit)
       return fail(DPP_ERR_WORKSPACE,
                   "workspace cap too small: one q tile needs " +
-                      std::to_string(need * (c.head_dim + 1) * 4 + header_bytes) + " B");
+                      std::to_string(need * (c.head_dim + 1) * 4 + header_bytes_max) + " B");
     if (used + need > slot_limit) {
       ++pass;
       used = 0;
@@ -247,7 +324,25 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     plan->merge_pass.push_back((int32_t)merges.size());
   }
 
-  // Serialise: preamble | requests | items | merges.
+  // Persistent chains for the wide launches, where two page tables fit beside the ring.
+  const bool chains_fit =
+      ring_bytes_for(c.head_dim) + 2 * page_table_bytes(max_page_span, c.head_dim) + kOutStageBytes <= (int64_t)kLdsLimit;
+  std::vector<UnitRecord> units;
+  plan->chain_offset.assign((size_t)num_passes, -1);
+  plan->chain_blocks.assign((size_t)num_passes, 0);
+  const int32_t unit_offset = kHeaderWords + 4 * batch_size + kItemWords * (int32_t)n_items + 4 * (int32_t)n_merges;
+  for (int32_t p = 0; p < num_passes && chain_kind && chains_fit; ++p) {
+    const int32_t b0 = plan->item_pass[(size_t)p], b1 = plan->item_narrow[(size_t)p];
+    if (b1 <= b0) continue;
+    std::vector<UnitRecord> r = build_chains(items.data() + b0, b1 - b0, c.num_kv_heads, p);
+    plan->chain_offset[(size_t)p] = unit_offset + kItemWords * (int32_t)units.size();
+    plan->chain_blocks[(size_t)p] = (int32_t)std::min<int64_t>(r.size(), kPersistentBlocks);
+    units.insert(units.end(), r.begin(), r.end());
+  }
+  const int64_t words = unit_offset + kItemWords * (int64_t)units.size();
+  const size_t header_bytes = align_up((size_t)words * 4, 256);
+
+  // Serialise: preamble | requests | items | merges | unit records.
   plan->header.assign((size_t)words, 0);
   HeaderPreamble pre{};
   pre.magic = kHeaderMagic;
@@ -257,6 +352,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   pre.request_offset = kHeaderWords;
   pre.item_offset = kHeaderWords + 4 * batch_size;
   pre.merge_offset = pre.item_offset + kItemWords * (int32_t)n_items;
+  pre.unit_offset = units.empty() ? 0 : unit_offset;
+  pre.num_units = (int32_t)units.size();
   {
     // ids differ between plans of one process; mixing in the address makes a header left
     // behind by another process unlikely to match either
@@ -273,6 +370,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     std::memcpy(plan->header.data() + pre.item_offset, items.data(), items.size() * sizeof(PrefillItem));
   if (!merges.empty())
     std::memcpy(plan->header.data() + pre.merge_offset, merges.data(), merges.size() * sizeof(MergeItem));
+  if (!units.empty())
+    std::memcpy(plan->header.data() + unit_offset, units.data(), units.size() * sizeof(UnitRecord));
 
   plan->max_partial_slots = max_used;
   plan->header_bytes = header_bytes;

@@ -29,6 +29,10 @@ struct dpp_plan {
   // Pass p runs items [item_pass[p], item_narrow[p]) on the wide kernel and
   // [item_narrow[p], item_pass[p+1]) on the narrow one (one of the two ranges is empty).
   std::vector<int32_t> item_narrow;
+  // Pass p's wide launch is persistent if chain_offset[p] >= 0: chain_blocks[p] workgroups
+  // over the unit records at that word offset of the header.
+  std::vector<int32_t> chain_offset;
+  std::vector<int32_t> chain_blocks;
 
   int64_t max_partial_slots = 0;
   size_t header_bytes = 0;

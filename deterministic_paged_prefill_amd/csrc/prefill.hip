@@ -53,6 +53,7 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 #define DPP_LDS __attribute__((address_space(3)))
+#define DPP_GLOBAL __attribute__((address_space(1)))
 
 constexpr float kLn2 = 0.693147180559945309417f;
 // Rebase threshold of the online softmax's reference max, in log2 units (P_j <= 2^8).
@@ -80,6 +81,7 @@ struct Geo {
   static constexpr int NCH = BN * CH / THREADS;    // 16-byte chunks per thread per tensor per tile
   static constexpr int KPI = 64 * 16 / ROW_BYTES;  // key rows one wave-wide DMA load covers
   static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
+  static_assert(LDS_BYTES == ring_bytes_for(D), "ring size");
   // narrow bf16 kernel: P^T and alpha of two tiles, then l and m, passed between two waves
   static constexpr int XSLOT = 64 * KC * 16 + 64 * 4;
   static constexpr int XBYTES = 2 * XSLOT + 2 * 64 * 4;
@@ -166,6 +168,13 @@ __device__ inline void dma16(const void* gaddr, uint32_t lds_base) {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
+// A wave-uniform 64-bit value held in scalar registers (the inline assembly below takes its
+// descriptors in scalar registers).
+__device__ inline uint64_t uniform64(uint64_t x) {
+  return (uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)x) |
+         ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(x >> 32)) << 32);
+}
+
 // Raw buffer descriptor (stride 0: num_records counts bytes) over [base, base + bytes); a
 // load at an offset past `bytes` returns zeros.
 __device__ inline i32x4 buffer_rsrc(uint64_t base, uint32_t bytes) {
@@ -174,10 +183,23 @@ __device__ inline i32x4 buffer_rsrc(uint64_t base, uint32_t bytes) {
 
 // LDS-DMA through a buffer descriptor: lane l fetches 16 bytes at descriptor offset
 // voff (zeros past num_records) and they land at LDS byte address lds_base + 16 l.
+__device__ inline i32x4 uniform_rsrc(i32x4 r) {
+  return i32x4{__builtin_amdgcn_readfirstlane(r[0]), __builtin_amdgcn_readfirstlane(r[1]),
+               __builtin_amdgcn_readfirstlane(r[2]), __builtin_amdgcn_readfirstlane(r[3])};
+}
+// (rsrc and lds_base are wave-uniform; readfirstlane only states it to the compiler)
 __device__ inline void dma16_buf(int voff, i32x4 rsrc, uint32_t lds_base) {
   asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds"
                :
-               : "v"(voff), "s"(rsrc), "s"(lds_base)
+               : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+               : "memory");
+}
+
+// Same with 4 bytes a lane, landing at lds_base + 4 l.
+__device__ inline void dma4_buf(int voff, i32x4 rsrc, uint32_t lds_base) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dword %0, %1, 0 offen lds"
+               :
+               : "v"(voff), "s"(uniform_rsrc(rsrc)), "s"(__builtin_amdgcn_readfirstlane(lds_base))
                : "memory");
 }
 
@@ -203,108 +225,175 @@ template <int D, bool FP8, int NB, int MODE>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
   using C = Geo<D, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  // page table of the item: page ids (-1 = bad id), or in scalar mode the pages' byte offsets
   // Narrow bf16 kernel with eight waves: wave 0 computes scores and softmax, wave 4 (on the
   // same SIMD) the output, and waves 2, 3, 6, 7 issue the DMA loads.
   constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
+  // Two-group schedule (see below): bf16 wide tiles with two waves per SIMD. Its launches may
+  // be persistent (a chain of units per workgroup).
+  constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
   unsigned char* xb = smem + C::LDS_BYTES;  // exchange buffer (kSpec)
-  unsigned char* pt = xb + (kSpec ? C::XBYTES : 0);
-  int32_t* pg_lds = reinterpret_cast<int32_t*>(pt);
-  int64_t* pg_off = reinterpret_cast<int64_t*>(pt);
+  // page-id tables after the ring: raw ids from kv_indices, 4 bytes an entry; a persistent
+  // launch alternates between two (the next unit's ids load during the current unit)
+  unsigned char* pt0 = xb + (kSpec ? C::XBYTES : 0);
+  const int pt_bytes = (int)page_table_bytes(a.page_slots, D);
+  int32_t* pg_lds = reinterpret_cast<int32_t*>(pt0);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: scalar branches below
-  // Work w = kvh * num_items + item. The dispatcher hands block b to XCD b % kXcds; giving
-  // each XCD one contiguous range of w keeps the q tiles that read one request's KV for one
-  // kv head on the same L2.
-  const int w = xcd_chunked(blockIdx.x, a.num_items * a.num_kv_heads);
-  const int kvh = w / a.num_items;
+  constexpr int kElem = FP8 ? 1 : 2;
 
-  // The item record (with its request's descriptor) and the preamble are read together; the
-  // record lies inside the workspace whatever the header holds.
+  // ---- the unit (item, kv head) record: word k in lane k of one register, read into scalar
+  // registers by decode. A persistent launch starts workgroup b at record b of its chain
+  // records; otherwise work w = kvh * num_items + item goes to block b with w =
+  // xcd_chunked(b, n): the dispatcher hands block b to XCD b % kXcds, and each XCD then
+  // receives one contiguous range of w (the q tiles that read one request's KV for one kv
+  // head share an L2).
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
-  const PrefillItem it =
-      reinterpret_cast<const PrefillItem*>(a.header + a.item_offset)[a.item_begin + (w - kvh * a.num_items)];
-  if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
-  const RequestDesc rq = it.req;
+  const bool chained = a.chain_offset >= 0;
+  auto fetch_record = [&](int idx) -> int32_t {
+    const int32_t* r = a.header + a.chain_offset + idx * kItemWords;
+    return lane < kItemWords ? r[lane] : 0;
+  };
+  int32_t rv;
+  if (chained) {
+    rv = fetch_record(blockIdx.x);
+  } else {
+    const int w = xcd_chunked(blockIdx.x, a.num_items * a.num_kv_heads);
+    const int h = w / a.num_items;
+    const int32_t* r = a.header + a.item_offset + (a.item_begin + (w - h * a.num_items)) * kItemWords;
+    rv = lane < kItemWords ? r[lane] : 0;
+    rv = lane == 7 ? -1 : (lane == 12 ? h : rv);  // the unit record's next and kv_head words
+  }
+  const uint32_t magic = pre->magic, plan_id = pre->plan_id;  // one round trip for both
+  if ((magic != kHeaderMagic) | (plan_id != a.plan_id)) return;  // not this plan's work list
+  auto decode = [&](int32_t v) {
+    UnitRecord u;
+    u.request = __builtin_amdgcn_readlane(v, 0);
+    u.row_start = __builtin_amdgcn_readlane(v, 1);
+    u.split = __builtin_amdgcn_readlane(v, 2);
+    u.tile_splits = __builtin_amdgcn_readlane(v, 3);
+    u.kv_tile_begin = __builtin_amdgcn_readlane(v, 4);
+    u.kv_tile_end = __builtin_amdgcn_readlane(v, 5);
+    u.slot_base = __builtin_amdgcn_readlane(v, 6);
+    u.next = __builtin_amdgcn_readlane(v, 7);
+    u.req.q_start = __builtin_amdgcn_readlane(v, 8);
+    u.req.qo_len = __builtin_amdgcn_readlane(v, 9);
+    u.req.page_start = __builtin_amdgcn_readlane(v, 10);
+    u.req.kv_len = __builtin_amdgcn_readlane(v, 11);
+    u.kv_head = __builtin_amdgcn_readlane(v, 12);
+    u.block = u.pass = u.pad = 0;
+    return u;
+  };
 
   const int g = a.group;
-  const int tile_rows = min(C::PLAN_BM, rq.qo_len * g - it.row_start);
-  const int ctx = rq.kv_len - rq.qo_len;  // position of query token 0
   const int lg = lane >> 4;                // 16-lane group: 8-wide k slice in, 4 output rows out
   const int li = lane & 15;                // column (query row) within a 16-row block
-  const int split_key0 = it.split * kSplitTokens;
   const int row_wave = kSpec ? 0 : wave;  // whose 16-row blocks this wave works on
-  const bool has_rows = row_wave * C::RPW < tile_rows;  // wave-uniform
-  const bool s_rows = has_rows && (!kSpec || wave == 0);  // scores and softmax
-  const bool o_rows = has_rows && (!kSpec || wave == 4);  // output
-
-  // Rows of this lane: tile-local packed row lr = RPW*wave + 16*nb + li.
-  int p_row[NB];  // position of the row (INT_MAX past the tile: no key is masked)
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int lr = row_wave * C::RPW + nb * 16 + li;
-    p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
-  }
-  const int p_min = ctx + it.row_start / g;
-
-  // ---- page ids of the keys this item visits -> LDS
   const int page_size = a.page_size;
   const int page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz(page_size) : -1;
-  const int kt0 = it.kv_tile_begin;
-  const int n_tiles = it.kv_tile_end - kt0;  // >= 1
-  const int key_lo = kt0 * C::BN;
-  const int key_hi = min(it.kv_tile_end * C::BN, rq.kv_len);
-  const int key_lo_page = key_lo / page_size;
-  const int n_pages = key_hi > key_lo ? (key_hi - 1) / page_size - key_lo_page + 1 : 0;
-  for (int i = tid; i < n_pages; i += C::THREADS) {
-    const int32_t id = a.kv_indices[rq.page_start + key_lo_page + i];
-    const bool good = id >= 0 && id < a.num_pages;
-    if constexpr (MODE == kPagesScalar)
-      pg_off[i] = good ? (int64_t)id * ((int64_t)a.num_kv_heads * D * 2 * page_size) : -1;
-    else
-      pg_lds[i] = good ? id : -1;
-  }
+  const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElem;
+  const int64_t page_bytes = token_bytes * page_size;
+
+  // ---- state of the current unit
+  int kvh, cur_next;
+  PrefillItem it;
+  RequestDesc rq;
+  int tile_rows, ctx, split_key0, p_min, kt0, n_tiles, key_lo_page, n_pages;
+  bool has_rows, s_rows, o_rows;
+  int p_row[NB];  // position of the lane's rows (INT_MAX past the tile: no key is masked)
+  const unsigned char* kbase;  // the unit's kv head inside the K and V pools
+  const unsigned char* vbase;
+  // pages [lo, lo + n) of request u.req hold keys [kv_tile_begin BN, min(kv_tile_end BN, kv_len))
+  auto page_span = [&](const UnitRecord& u, int& lo, int& n) {
+    const int key_lo = u.kv_tile_begin * C::BN;
+    const int key_hi = min(u.kv_tile_end * C::BN, u.req.kv_len);
+    lo = key_lo / page_size;
+    n = key_hi > key_lo ? (key_hi - 1) / page_size - lo + 1 : 0;
+  };
+  auto set_unit = [&](const UnitRecord& u) {
+    kvh = u.kv_head;
+    cur_next = u.next;
+    it.request = u.request;
+    it.row_start = u.row_start;
+    it.split = u.split;
+    it.tile_splits = u.tile_splits;
+    it.kv_tile_begin = u.kv_tile_begin;
+    it.kv_tile_end = u.kv_tile_end;
+    it.slot_base = u.slot_base;
+    rq = u.req;
+    tile_rows = min(C::PLAN_BM, rq.qo_len * g - it.row_start);
+    ctx = rq.kv_len - rq.qo_len;  // position of query token 0
+    split_key0 = it.split * kSplitTokens;
+    has_rows = row_wave * C::RPW < tile_rows;  // wave-uniform
+    s_rows = has_rows && (!kSpec || wave == 0);  // scores and softmax
+    o_rows = has_rows && (!kSpec || wave == 4);  // output
+    // Rows of this lane: tile-local packed row lr = RPW*wave + 16*nb + li.
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int lr = row_wave * C::RPW + nb * 16 + li;
+      p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
+    }
+    p_min = ctx + it.row_start / g;
+    kt0 = it.kv_tile_begin;
+    n_tiles = it.kv_tile_end - kt0;  // >= 1
+    page_span(u, key_lo_page, n_pages);
+    kbase = reinterpret_cast<const unsigned char*>(a.k_pool) + (int64_t)kvh * D * kElem;
+    vbase = reinterpret_cast<const unsigned char*>(a.v_pool) + (int64_t)kvh * D * kElem;
+  };
+  UnitRecord first = decode(rv);
+  set_unit(first);
+
+  // ---- page ids of a unit -> LDS table, by DMA (lane l of load c brings entry 64c + l;
+  // entries past the unit's pages read as 0 and are never used)
+  auto load_page_ids = [&](const UnitRecord& u, int32_t* table) {
+    int lo, n;
+    page_span(u, lo, n);
+    const uint64_t src = reinterpret_cast<uint64_t>(a.kv_indices + u.req.page_start + lo);
+    const i32x4 rsrc = buffer_rsrc(uniform64(src), (uint32_t)__builtin_amdgcn_readfirstlane(n * 4));
+    const uint32_t t0 = (uint32_t)(uintptr_t)table;
+    for (int c = wave; c * 64 < n; c += C::WAVES) dma4_buf((c * 64 + lane) * 4, rsrc, t0 + (uint32_t)c * 256u);
+  };
+  load_page_ids(first, pg_lds);
 
   // ---- query rows as the QK^T B operand: lane (lg, li) holds head_dim [32dc + 8lg, +8)
   bf16x8 qreg[NB][C::DC];
+  auto load_q = [&]() {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int lr = row_wave * C::RPW + nb * 16 + li;
-    const bool valid = lr < tile_rows && s_rows;
-    const int R = it.row_start + lr;
-    const int token = R / g;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                         ((int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g)) * D + 8 * lg;
+    for (int nb = 0; nb < NB; ++nb) {
+      const int lr = row_wave * C::RPW + nb * 16 + li;
+      const bool valid = lr < tile_rows && s_rows;
+      const int R = it.row_start + lr;
+      const int token = R / g;
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g)) * D + 8 * lg;
 #pragma unroll
-    for (int dc = 0; dc < C::DC; ++dc) {
-      u32x4 v = u32x4{0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4*>(qp + dc * 32);
-      qreg[nb][dc] = __builtin_bit_cast(bf16x8, v);
+      for (int dc = 0; dc < C::DC; ++dc) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (valid) v = *reinterpret_cast<const u32x4*>(qp + dc * 32);
+        qreg[nb][dc] = __builtin_bit_cast(bf16x8, v);
+      }
     }
+  };
+  if constexpr (!kPP) {
+    load_q();
+    // Q and the page ids in registers and LDS before any DMA load of K or V is issued: a wait
+    // for them inside the loop would also wait for every DMA load in flight
+    wait_vmcnt<0>();
+    __syncthreads();  // page table visible
   }
-  // Q and the page ids in registers before any DMA load is issued: a wait for them inside
-  // the loop would also wait for every DMA load in flight
-  wait_vmcnt<0>();
-  __syncthreads();  // page table visible
 
   // ---- gather. Chunk i (0 <= i < NCH) of this thread in every KV tile is a fixed 16-byte
   // piece of a fixed key row; only the page it sits on changes from tile to tile. A chunk
   // past kv_len, of a tile outside the item, or on a page id outside the pool reads 16 zero
-  // bytes from the preamble's reserved words instead: the loads never branch, so their
+  // bytes from the preamble's zero chunk instead: the loads never branch, so their
   // number per tile is fixed.
   //   bf16: the chunks of one wave's DMA load are the 64 consecutive LDS chunks
   //         [64 (i WAVES + wave), +64); the global chunk is chosen so that it lands in its
   //         swizzled slot.
   //   fp8:  chunk q = tid + THREADS i, loaded to registers, decoded, stored to its slot.
-  constexpr int kElem = FP8 ? 1 : 2;
-  const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElem;
-  const int64_t page_bytes = token_bytes * page_size;
   constexpr bool pow2_pages = MODE != kPagesGeneral;
   static_assert(!(FP8 && MODE == kPagesScalar), "fp8 stages through registers");
-  // Two-group schedule (see below): bf16 wide tiles with two waves per SIMD.
-  constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
   // Waves that issue DMA loads: 2, 3, 6, 7 in the narrow bf16 kernel, otherwise all.
   constexpr int IW = kSpec ? 4 : C::WAVES;
   const int iw = kSpec ? ((wave & 1) | ((wave >> 2) << 1)) : wave;  // index among the issuers
@@ -312,11 +401,9 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   constexpr int NL = C::TILE_BYTES / (IW * 1024);         // their loads per tensor per tile
   constexpr int NCHT = FP8 ? C::NCH : NL;                 // chunks per thread per tensor per tile
   constexpr int KA = kPP ? 3 : C::NBUF;                   // load group t brings K(t + KA), V(t + 2)
-  const unsigned char* zero16 = reinterpret_cast<const unsigned char*>(pre->reserved);
-  const unsigned char* kbase = reinterpret_cast<const unsigned char*>(a.k_pool);
-  const unsigned char* vbase = reinterpret_cast<const unsigned char*>(a.v_pool);
+  const unsigned char* zero16 = reinterpret_cast<const unsigned char*>(pre->zero_chunk);
   int krow[NCHT];        // key row inside the tile
-  int kcol[NCHT];        // byte offset of the K chunk inside a token's row of the pool
+  int kcol[NCHT];        // byte offset of the K chunk inside the kv head's part of a token row
   int vcol[NCHT];        // same for V
   int lds_k[NCHT];       // fp8: LDS byte offset of the decoded K chunk (V: lds_v)
   int lds_v[NCHT];
@@ -339,8 +426,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       c_v = slot ^ ((krow[i] & 7) << 1);   // chunk_off_v(key, c_v) == 16 q
       lds_k[i] = lds_v[i] = 0;
     }
-    kcol[i] = (kvh * D + c_k * 8) * kElem;
-    vcol[i] = (kvh * D + c_v * 8) * kElem;
+    kcol[i] = c_k * 8 * kElem;
+    vcol[i] = c_v * 8 * kElem;
     pg_rel[i] = MODE == kPagesPow2 ? (krow[i] >> page_shift) : 0;
     in_page[i] = MODE == kPagesPow2 ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
   }
@@ -365,7 +452,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       pid = pg_lds[pi - key_lo_page];
       inpg = (int64_t)(kk - pi * page_size) * token_bytes;
     }
-    const bool ok = t >= 0 && t < n_tiles && key < rq.kv_len && pid >= 0;
+    const bool ok = t >= 0 && t < n_tiles && key < rq.kv_len && pid >= 0 && pid < a.num_pages;
     return ok ? base + (pid * page_bytes + inpg + col) : zero16;
   };
 
@@ -393,7 +480,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       for (int i = 0; i < NCHT; ++i) pid[i] = pg_lds[tp + pg_rel[i]];
 #pragma unroll
       for (int i = 0; i < NCHT; ++i) {
-        const bool ok = krow[i] < lim && pid[i] >= 0;
+        const bool ok = krow[i] < lim && pid[i] >= 0 && pid[i] < a.num_pages;
         const uint64_t off = (uint64_t)(uint32_t)(ok ? pid[i] : 0) * (uint64_t)page_bytes +
                              (uint64_t)in_page[i] + (uint64_t)(v ? vcol[i] : kcol[i]);
         dma16(ok ? base + off : zero16, buf + (uint32_t)((i * IW + iw) * 1024));
@@ -433,12 +520,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     const int key0 = kt * C::BN + (i * IW + iw) * C::KPI;
     return min((key0 >> page_shift) - key_lo_page, n_pages - 1);
   };
-  int64_t ids[2][NCHT];  // page byte offsets of the next group's K and V loads (uniform values)
+  int32_t ids[2][NCHT];  // page ids of the next group's K and V loads (uniform values)
   auto read_ids = [&](int g) {
 #pragma unroll
     for (int i = 0; i < NCHT; ++i) {
-      ids[0][i] = pg_off[page_slot(g + KA, i)];
-      ids[1][i] = pg_off[page_slot(g + 2, i)];
+      ids[0][i] = pg_lds[page_slot(g + KA, i)];
+      ids[1][i] = pg_lds[page_slot(g + 2, i)];
     }
   };
   // Descriptors of the next group's loads, prepared ahead so that firing a load is an M0
@@ -449,23 +536,23 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   };
   constexpr int kLoads = 2 * NCHT;
   LoadDesc nd[kLoads];
-  auto prep = [&](int g) {  // from ids (group g's page offsets)
+  auto prep = [&](int grp) {  // from ids (group grp's page ids)
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
       const bool v = j >= NCHT;
       const int i = v ? j - NCHT : j;
-      const int t = v ? g + 2 : g + KA;
-      const int64_t off_lds = ids[v ? 1 : 0][i];
+      const int t = v ? grp + 2 : grp + KA;
+      const int id = __builtin_amdgcn_readfirstlane(ids[v ? 1 : 0][i]);
+      const bool good = id >= 0 && id < a.num_pages;  // else the load reads zeros
       const uint64_t base = reinterpret_cast<uint64_t>(v ? vbase : kbase);
       const bool tile_ok = t >= 0 && t < n_tiles;
       const int key0 = (kt0 + min(max(t, 0), n_tiles - 1)) * C::BN + (i * IW + iw) * C::KPI;
-      const int64_t off = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)off_lds)) |
-                                    ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(off_lds >> 32)) << 32));
+      const uint64_t off = good ? (uint64_t)(uint32_t)id * (uint64_t)page_bytes : 0;
       const int rows = min(max(rq.kv_len - key0, 0), C::KPI);
       const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane(
-          (int)((tile_ok && off >= 0) ? (uint32_t)rows * (uint32_t)token_bytes : 0u));
-      const uint64_t addr = base + (uint64_t)off + (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
-      nd[j].rsrc = buffer_rsrc(addr, bytes);
+          (int)((tile_ok && good) ? (uint32_t)rows * (uint32_t)token_bytes : 0u));
+      const uint64_t addr = base + off + (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
+      nd[j].rsrc = buffer_rsrc(uniform64(addr), bytes);
       nd[j].lds = lds0 + (uint32_t)(((v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES + (i * IW + iw) * 1024);
     }
   };
@@ -486,13 +573,106 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const float c = a.scale_log2;
   float m_sc[NB], l_sum[NB];  // reference max (scaled, base 2) and running sum per row
   f32x4 acc[C::DB][NB];
+  auto reset_state = [&]() {
 #pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    m_sc[nb] = -INFINITY;
-    l_sum[nb] = 0.f;
+    for (int nb = 0; nb < NB; ++nb) {
+      m_sc[nb] = -INFINITY;
+      l_sum[nb] = 0.f;
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+      for (int db = 0; db < C::DB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  reset_state();
+
+  // ---- output of a unit: lane holds O^T[d = 16db + 4lg + j][row 16nb + li]. The unit is
+  // given by its record register, so that a wave can write a unit's rows after the next unit
+  // has begun.
+  // Output pointers as scalar values in the global address space: the two row kinds below
+  // store through different pointers under a per-lane condition, and a per-lane choice
+  // between two kernel-argument fields would be a per-lane load (whose wait would also wait
+  // for every DMA load in flight). Generic pointers would make flat stores, which the LDS
+  // counter also tracks: every later LDS wait would wait for them to reach memory.
+  DPP_GLOBAL uint16_t* const o_out = (DPP_GLOBAL uint16_t*)uniform64(reinterpret_cast<uint64_t>(a.o));
+  DPP_GLOBAL float* const lse_out = (DPP_GLOBAL float*)uniform64(reinterpret_cast<uint64_t>(a.lse));
+  DPP_GLOBAL float* const part_o_out = (DPP_GLOBAL float*)uniform64(reinterpret_cast<uint64_t>(a.part_o));
+  DPP_GLOBAL float* const part_lse_out = (DPP_GLOBAL float*)uniform64(reinterpret_cast<uint64_t>(a.part_lse2));
+  // Rows of the last split (p < 4096) leave as bf16. In the two-group schedule they pass
+  // through 2 KiB of LDS per wave (after the page tables; one group writes at a time, beside
+  // the other group's loop): 16 rows x 64 head_dim values at a time are written in the MFMA
+  // layout and read back as 16-byte pieces of 8 rows, so that every store covers whole
+  // 128-byte lines (a store straight from the MFMA layout writes 16 rows x 32 bytes), which
+  // the next unit's loads then queue behind for less time. 16-byte chunk c of staged row r
+  // sits at chunk c ^ (r % 8). The other schedules end their workgroup with the writes and
+  // store straight from the MFMA layout.
+  constexpr int kStageBytes = 2048;
+  unsigned char* const stage = pt0 + (chained ? 2 : 1) * pt_bytes + (wave & 3) * kStageBytes;
+  auto write_out = [&](int32_t rec) {
+    const UnitRecord e = decode(rec);
+    const int e_rows = min(C::PLAN_BM, e.req.qo_len * g - e.row_start);
+    const int e_ctx = e.req.kv_len - e.req.qo_len;
+    const int e_key0 = e.split * kSplitTokens;
+    // output row (packed row R of the request) in o and lse
+    auto out_row = [&](int lr) {
+      const int R = e.row_start + lr;
+      const int token = R / g;
+      return (int64_t)(e.req.q_start + token) * a.num_qo_heads + e.kv_head * g + (R - token * g);
+    };
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int lr = row_wave * C::RPW + nb * 16 + li;  // the row this lane holds
+      const int p = lr < e_rows ? e_ctx + (e.row_start + lr) / g : -1;
+      const bool mine = p >= e_key0;                   // a row of this split
+      const float inv_l = 1.f / l_sum[nb];
+      const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l_sum[nb]);
+      if (mine && p < kSplitTokens) {
+        const int64_t orow = out_row(lr);
+        if (lg == 0) lse_out[orow] = lse2 * kLn2;
+        if constexpr (!kPP) {
+          DPP_GLOBAL uint16_t* op = o_out + orow * D + 4 * lg;
+#pragma unroll
+          for (int db = 0; db < C::DB; ++db)
+            *reinterpret_cast<DPP_GLOBAL u32x2*>(op + db * 16) =
+                u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
+                      pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
+        }
+      } else if (mine) {
+        // a row reaching past the first split: its fp32 partial, straight from the MFMA layout
+        const int64_t slot = partial_slot(e.slot_base, e.tile_splits, e.kv_head, e.split, lr, C::PLAN_BM);
+        DPP_GLOBAL float* pp = part_o_out + slot * D + 4 * lg;
+#pragma unroll
+        for (int db = 0; db < C::DB; ++db)
+          *reinterpret_cast<DPP_GLOBAL f32x4*>(pp + db * 16) =
+              f32x4{acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l, acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l};
+        if (lg == 0) part_lse_out[slot] = lse2;
+      }
+      if constexpr (kPP) {
+#pragma unroll
+      for (int sp = 0; sp < C::DB / 4; ++sp) {  // head_dim [64 sp, +64)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int db = 4 * sp + k;
+          const int c = (2 * k + (lg >> 1)) ^ (li & 7);
+          *reinterpret_cast<DPP_LDS u32x2*>((DPP_LDS unsigned char*)stage + li * 128 + c * 16 + (lg & 1) * 8) =
+              u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
+                    pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
+        }
+        asm volatile("" ::: "memory");  // the wave's own LDS writes, then its reads (in order)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int r = 8 * h + (lane >> 3);  // staged row, 16-byte piece kk of its 128 bytes
+          const int kk = lane & 7;
+          const u32x4 v = *reinterpret_cast<const DPP_LDS u32x4*>((const DPP_LDS unsigned char*)stage + r * 128 +
+                                                                  ((kk ^ (r & 7)) << 4));
+          const int rlr = row_wave * C::RPW + nb * 16 + r;
+          const int rp = rlr < e_rows ? e_ctx + (e.row_start + rlr) / g : -1;
+          if (rp >= e_key0 && rp < kSplitTokens)
+            *reinterpret_cast<DPP_GLOBAL u32x4*>(o_out + out_row(rlr) * D + 64 * sp + 8 * kk) = v;
+        }
+        asm volatile("" ::: "memory");
+      }
+      }
+    }
+  };
 
   constexpr int kAhead = ahead_for<NB>();
   constexpr bool kPin = kPP || NB == 1;  // pin the read-ahead order (the scheduler undoes it)
@@ -776,105 +956,124 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     // A(t-2), one phase before any wave issues group t (in its A(t-1)). Groups -3..0 are
     // issued up front. Per row the sequence is the plain one: O = alpha(t) O, then
     // O += PV(t).
+    //
+    // A persistent workgroup runs its chain of units back to back. The leading waves write a
+    // unit's rows while the trailing waves run its last PV; the trailing waves write theirs
+    // while the next unit's Q and first load group arrive. The next unit's record and page
+    // ids are fetched one unit ahead (ids into the other LDS table).
     const bool leading = wave < C::WAVES / 2;
-    if constexpr (MODE == kPagesScalar) {
-      read_ids(-3);
-#pragma unroll
-      for (int g = -3; g <= 0; ++g) {
-        prep(g);
-#pragma unroll
-        for (int j = 0; j < kLoads; ++j) fire(j);
-        read_ids(g + 1);
-      }
-    } else {
-#pragma unroll
-      for (int g = -3; g <= 0; ++g) issue(g);
-    }
-    wait_vmcnt<3 * kGroupLoads>();  // group -3 landed: K(0), V(-1)
-    __syncthreads();
-    if (has_rows) qk(s, 0);
-    if (!leading) {
-      wait_vmcnt<2 * kGroupLoads>();  // group -2 (K(1), V(0)) before the leading group's A(0)
-      __syncthreads();
-    }
+    int tab = 0;  // page table of the current unit
+    // records (one word a lane): current unit, the next one, and the one after it (arriving).
+    // They move on right after the full wait at the start of a unit, so that no copy of a
+    // register still being loaded needs a wait of its own.
+    int32_t rcur = rv, rnext = 0, rfetch = 0;
+    bool has_prev = false, rotate = false;
+    if (cur_next >= 0) rnext = fetch_record(cur_next);
+    wait_vmcnt<0>();
+    __syncthreads();  // the first unit's page ids visible
     // group g's loads are prepared in B(g-1) and fired between the PV steps of A(g-1)
     constexpr int kEvery = (C::KC * C::DB) / kLoads;
     static_assert(kEvery >= 1, "one load per PV step at most");
-    for (int t = 0; t < n_tiles; ++t) {
-      if (has_rows) {
-        if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
-        float alpha[NB];
-        softmax(s, pb, alpha, std::true_type{});
-      }
-      if constexpr (MODE == kPagesScalar) prep(t + 1);
-      // A(t) reads group t-2; the leading group's A(t) starts at the next barrier, the
-      // trailing group's one phase later (its wait for group t-1 follows its A(t))
-      if (leading) wait_vmcnt<2 * kGroupLoads>();
-      __syncthreads();
+    for (;;) {
+      // Q and load group -3 (K(0)); the trailing waves' rows of the previous unit
+      load_q();
       if constexpr (MODE == kPagesScalar) {
-        if (has_rows) {
-          pv_acc(pb, t, [&](int st) {
-            if (st % kEvery == 0 && st / kEvery < kLoads) fire(st / kEvery);
-          });
-        } else {
-#pragma unroll
-          for (int j = 0; j < kLoads; ++j) fire(j);
-        }
-        read_ids(t + 2);
+        read_ids(-3);
+        issue_group_scalar(-3);
       } else {
-        issue(t + 1);
-        if (has_rows) pv_acc(pb, t, no_hook);
+        issue(-3);
       }
-      if (has_rows && t + 1 < n_tiles) qk(s, t + 1);
-      if (!leading) wait_vmcnt<2 * kGroupLoads>();  // group t-1, for the leading group's A(t+1)
+      if (!leading && has_prev) {
+        write_out(rcur);  // still the previous unit's record
+        reset_state();
+      }
+      wait_vmcnt<0>();
       __syncthreads();
+      if (rotate) {
+        rcur = rnext;
+        rnext = rfetch;
+      }
+      // the next unit's page ids and the record after it (older than the groups below, so the
+      // counted waits cover them), then groups -2..0
+      const bool has_next = cur_next >= 0;
+      if (has_next) {
+        const UnitRecord nxt = decode(rnext);
+        load_page_ids(nxt, reinterpret_cast<int32_t*>(pt0 + (tab ^ 1) * pt_bytes));
+        if (nxt.next >= 0) rfetch = fetch_record(nxt.next);
+      }
+#pragma unroll
+      for (int grp = -2; grp <= 0; ++grp) issue(grp);
+      if (has_rows) qk(s, 0);
+      if (!leading) {
+        wait_vmcnt<2 * kGroupLoads>();  // group -2 (K(1), V(0)) before the leading group's A(0)
+        __syncthreads();
+      }
+      for (int t = 0; t < n_tiles; ++t) {
+        if (has_rows) {
+          if ((kt0 + t) * C::BN + C::BN - 1 > p_min) mask(s, t);
+          float alpha[NB];
+          softmax(s, pb, alpha, std::true_type{});
+        }
+        if constexpr (MODE == kPagesScalar) prep(t + 1);
+        // A(t) reads group t-2; the leading group's A(t) starts at the next barrier, the
+        // trailing group's one phase later (its wait for group t-1 follows its A(t))
+        if (leading) wait_vmcnt<2 * kGroupLoads>();
+        __syncthreads();
+        if constexpr (MODE == kPagesScalar) {
+          if (has_rows) {
+            pv_acc(pb, t, [&](int st) {
+              if (st % kEvery == 0 && st / kEvery < kLoads) fire(st / kEvery);
+            });
+          } else {
+#pragma unroll
+            for (int j = 0; j < kLoads; ++j) fire(j);
+          }
+          read_ids(t + 2);
+        } else {
+          issue(t + 1);
+          if (has_rows) pv_acc(pb, t, no_hook);
+        }
+        if (has_rows && t + 1 < n_tiles) qk(s, t + 1);
+        if (!leading) wait_vmcnt<2 * kGroupLoads>();  // group t-1, for the leading group's A(t+1)
+        __syncthreads();
+      }
+      // the leading waves' rows are final: write them during the trailing group's last A
+      if (leading) {
+        if (has_rows) write_out(rcur);
+        reset_state();
+        __syncthreads();
+      }
+      if (!has_next) {
+        if (!leading && has_rows) write_out(rcur);
+        break;
+      }
+      has_prev = !leading;
+      rotate = true;
+      set_unit(decode(rnext));
+      tab ^= 1;
+      pg_lds = reinterpret_cast<int32_t*>(pt0 + tab * pt_bytes);
     }
-    if (leading) __syncthreads();
   }
   wait_vmcnt<0>();  // no load may outlive the workgroup (a DMA load would land in LDS)
 
-  // ---- epilogue: lane holds O^T[d = 16db + 4lg + j][row 16nb + li]
-  if (!o_rows) return;
-#pragma unroll
-  for (int nb = 0; nb < NB; ++nb) {
-    const int lr = row_wave * C::RPW + nb * 16 + li;
-    const int p = p_row[nb];
-    if (lr >= tile_rows || p < split_key0) continue;  // not a row of this split
-    const int R = it.row_start + lr;
-    const int token = R / g;
-    const float inv_l = 1.f / l_sum[nb];
-    const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l_sum[nb]);
-    if (p / kSplitTokens == 0) {
-      const int64_t orow = (int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g);
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.o) + orow * D + 4 * lg;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        *reinterpret_cast<u32x2*>(op + db * 16) =
-            u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
-                  pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
-      if (lg == 0) a.lse[orow] = lse2 * kLn2;
-    } else {
-      const int64_t slot = partial_slot(it.slot_base, it.tile_splits, kvh, it.split, lr, C::PLAN_BM);
-      float* pp = a.part_o + slot * D + 4 * lg;
-#pragma unroll
-      for (int db = 0; db < C::DB; ++db)
-        *reinterpret_cast<f32x4*>(pp + db * 16) =
-            f32x4{acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l, acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l};
-      if (lg == 0) a.part_lse2[slot] = lse2;
-    }
+  // ---- epilogue (the two-group schedule writes its units' rows inside its chain loop)
+  if constexpr (!kPP) {
+    if (o_rows) write_out(rv);
   }
 }
 
 template <int D, bool FP8, int NB, int MODE>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   using C = Geo<D, NB>;
-  // page table: the item's pages plus one tile's worth of slack for the last tile's lookups
-  // past kv_len (their chunks read the zero chunk); byte offsets (8 bytes) in scalar mode,
-  // page ids (4 bytes) otherwise
-  constexpr size_t kEntry = MODE == kPagesScalar ? 8 : 4;
+  // page-id tables (4 bytes an entry): a unit's pages plus one tile's worth of slack for the
+  // last tile's lookups past kv_len (their chunks read the zero chunk); two in a persistent
+  // launch
   constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
-  const size_t lds = (size_t)C::LDS_BYTES + (kSpec ? C::XBYTES : 0) + ((size_t)a.page_slots + C::BN) * kEntry;
-  if (lds > 160 * 1024) return hipErrorInvalidValue;
+  const size_t pt_bytes = (size_t)page_table_bytes(a.page_slots, D);
+  constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
+  const size_t lds = (size_t)C::LDS_BYTES + (kSpec ? C::XBYTES : 0) + (a.chain_offset >= 0 ? 2 : 1) * pt_bytes +
+                     (kPP ? (size_t)kOutStageBytes : 0);
+  if (lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE>),
@@ -882,7 +1081,8 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
   }
-  dim3 grid((unsigned)(a.num_items * a.num_kv_heads));
+  dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains : a.num_items * a.num_kv_heads));
+  if (a.chain_offset >= 0 && !chained_launch(D, FP8, NB == 1)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
@@ -897,7 +1097,9 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   }
   // The narrow kernel's issuing waves compute nothing else: per-lane (vector) addresses
   // suit them. The wide kernel's waves are busy with the softmax: scalar descriptors.
-  if (NB > 1 && pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
+  if constexpr (NB > 1) {
+    if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
+  }
   return pow2 && P <= block_n_for(D) ? launch_one<D, false, NB, kPagesPow2>(a, stream)
                                      : launch_one<D, false, NB, kPagesGeneral>(a, stream);
 }

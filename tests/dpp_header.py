@@ -13,6 +13,8 @@ class ParsedPlan:
     items: np.ndarray     # [N, 16]: request, row_start, split, tile_splits, kv_tile_begin, kv_tile_end,
                           # slot_base, pad, then the request's q_start, qo_len, page_start, kv_len, pad x4
     merges: np.ndarray    # [M, 4]: request, row_start, tile_splits, slot_base
+    units: np.ndarray     # [U, 16]: persistent launches' unit records: the item's first 7 words,
+                          # next, the request's 4 words, kv_head, block, pass, pad
 
 
 def parse(words: np.ndarray) -> ParsedPlan:
@@ -22,4 +24,7 @@ def parse(words: np.ndarray) -> ParsedPlan:
     req = w[roff:roff + 4 * nreq].reshape(nreq, 4)
     items = w[ioff:ioff + 16 * nitems].reshape(nitems, 16)
     merges = w[moff:moff + 4 * nmerge].reshape(nmerge, 4)
-    return ParsedPlan(req, items, merges)
+    assert (w[8:12] == 0).all() and (w[14:16] == 0).all(), "zero chunk and reserved words"
+    uoff, nunits = int(w[12]), int(w[13])
+    units = w[uoff:uoff + 16 * nunits].reshape(nunits, 16)
+    return ParsedPlan(req, items, merges, units)

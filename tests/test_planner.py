@@ -143,7 +143,9 @@ def test_workspace_closed_form_single_pass(dpp):
             ntile += 1
             if S > 1:
                 slots += S * 8 * bm
-    words = 16 + 4 * len(specs) + 16 * len(parsed.items) + 4 * len(parsed.merges)
+    # every tile is wide: each (item, kv head) also has a unit record of the persistent launch
+    assert len(parsed.units) == 8 * len(parsed.items)
+    words = 16 + 4 * len(specs) + 16 * len(parsed.items) + 4 * len(parsed.merges) + 16 * len(parsed.units)
     hdr = _align(words * 4)
     assert p.info.header_bytes == hdr
     assert p.info.max_partial_slots == slots
@@ -166,6 +168,84 @@ def test_cap_bounds_workspace_and_adds_passes(dpp, cap_mib):
     # same work, only cut into passes
     key = lambda it: tuple(int(x) for x in it[:6])
     assert sorted(map(key, parse(p.header()).items)) == sorted(map(key, parse(unbounded.header()).items))
+
+
+def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
+    """The unit records of one persistent launch over `items` (its pass's items, launch order)."""
+    n = len(items)
+    n_units = n * hkv
+    assert len(units) == n_units
+    nb = min(n_units, blocks)
+    index = {tuple(int(x) for x in it[:3]): i for i, it in enumerate(items)}
+    cost = lambda rec: int(rec[5] - rec[4]) + 2
+    seen = np.zeros(n_units, dtype=bool)
+    covered = set()
+    load = {}
+    for b in range(nb):
+        assert units[b][13] == b, "workgroup b starts at record b"
+        k, costs = b, []
+        while k >= 0:
+            assert not seen[k], "a record reached twice"
+            seen[k] = True
+            rec = units[k]
+            assert rec[13] == b
+            i = index[tuple(int(x) for x in rec[:3])]
+            assert (rec[:7] == items[i][:7]).all() and (rec[8:12] == items[i][8:12]).all()
+            h = int(rec[12])
+            w = h * n + i
+            q, r = divmod(n_units, xcds)
+            x = next(x for x in range(xcds) if x * q + min(x, r) <= w < x * q + min(x, r) + q + (x < r))
+            assert b % xcds == x, "a unit runs on the XCD the plain launch order gives it"
+            covered.add((i, h))
+            c = cost(rec)
+            costs.append(c)
+            load[b] = load.get(b, 0) + c
+            k = int(rec[7])
+        # a chain is its units longest first, rotated: at most one cyclic ascent
+        ascents = sum(costs[j] < costs[(j + 1) % len(costs)] for j in range(len(costs)))
+        assert ascents <= 1, costs
+    assert seen.all(), "every record is on a chain"
+    assert covered == {(i, h) for i in range(n) for h in range(hkv)}
+    biggest = max(cost(u) for u in units)
+    for x in range(xcds):
+        loads = [load[b] for b in range(x, nb, xcds)]
+        if loads:
+            assert max(loads) - min(loads) <= biggest
+
+
+@pytest.mark.parametrize("specs", [[(1028, 1028)] * 16, [(67, 67)], [(1028, 1028)] * 2,
+                                   [(3700, 3700), (3701, 1), (4000, 300)], [(9000, 9000)],
+                                   [(1024 + t, t) for t in (1, 2, 3, 4)] * 4 + [(500, 500)]])
+def test_persistent_chains_cover_every_unit_once(dpp, specs):
+    parsed = parse(_plan(dpp, _specs_batch(specs)).header())
+    assert (parsed.units[:, 14] == 0).all()
+    _check_chains(parsed, parsed.items, parsed.units, 8)
+
+
+def test_persistent_chains_per_pass(dpp):
+    b = _specs_batch([(9000, 9000), (6000, 6000)])
+    p = _plan(dpp, b, cap=24 << 20)
+    assert p.info.num_passes > 1
+    parsed = parse(p.header())
+    # items of a pass are contiguous in the header and, with wide tiles only, all chained
+    seen = 0
+    for ps in range(p.info.num_passes):
+        units = parsed.units[parsed.units[:, 14] == ps]
+        n = len(units) // 8
+        _check_chains(parsed, parsed.items[seen:seen + n], units, 8)
+        seen += n
+    assert seen == len(parsed.items)
+
+
+def test_no_chains_where_not_persistent(dpp):
+    # narrow passes (extends), head_dim 256 and fp8 launches are not persistent
+    ext = _specs_batch([(1024 + t, t) for t in (1, 2, 3, 4)] * 4)
+    assert len(parse(_plan(dpp, ext).header()).units) == 0
+    big = _specs_batch([(1028, 1028)] * 2)
+    assert len(parse(_plan(dpp, big, hq=16, hkv=4, d=256).header()).units) == 0
+    assert len(parse(_plan(dpp, big, kv_dtype="fp8_e4m3", k_scale=1.0, v_scale=1.0).header()).units) == 0
+    # page size 1: two page tables of a 4096-key split do not fit beside the ring
+    assert len(parse(_plan(dpp, _specs_batch([(5000, 5000)], page=1), page=1).header()).units) == 0
 
 
 def test_zero_length_request_gets_no_rows(dpp):
