@@ -179,8 +179,8 @@ def main() -> int:
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark measures one GPU: the attention path is built "
-                                   "and measured on a single MI355X (see DESIGN.md for how it "
-                                   "would shard); run with --gpus 1"}))
+                                   "and measured on a single MI355X (it would shard by request, kv "
+                                   "head or KV split without changing a bit); run with --gpus 1"}))
         return 2
 
     import numpy as np
@@ -208,7 +208,7 @@ def main() -> int:
     # ---------------------------------------------------------------- extend (value)
     if args.only in (None, "extend"):
         log("building extend workload (distinct pages)")
-        work = wl.config2_extend_batch(layout="distinct")
+        work = wl.extend_batch(layout="distinct")
         cached, full = work.batches["cached"], work.batches["full"]
         run = Runner(work, cached, replicas=args.replicas)
         if args.only == "extend":  # profiler run: only the timed launches
@@ -238,7 +238,7 @@ def main() -> int:
                                 max_diff=max_diff, work=work, batch=cached,
                                 items=run.plan.info.num_prefill_items)
         # radix layout (prefix pages physically shared): logical bytes over a cache-served read
-        work_r = wl.config2_extend_batch(layout="radix")
+        work_r = wl.extend_batch(layout="radix")
         rr = Runner(work_r, work_r.batches["cached"], replicas=1)
         ms_r, _ = rr.timed(args.steps, args.warmup)
         result["extend"]["radix_logical_gbps"] = kv_bytes(work_r.batches["cached"], hkv, d, 2) / (ms_r * 1e-3) / 1e9
@@ -248,7 +248,7 @@ def main() -> int:
     # ---------------------------------------------------------------- cold prefill
     if args.only in (None, "prefill") and not args.no_prefill:
         log("building cold prefill workload")
-        work_p = wl.config3_cold_prefill()
+        work_p = wl.cold_prefill()
         bp = work_p.batches["full"]
         pr = Runner(work_p, bp, replicas=1)
         # A sustained matrix-core load takes ~100 launches (~25 ms) to reach its steady rate

@@ -10,7 +10,8 @@
 // combined by one thread group in a fixed order: no atomics, no dependence on how many rows
 // or tiles share the launch. Sources: fixed KV splits with partial-result buffers
 // (model-serving-minefield issue #73, correction comment, "What the flag actually does",
-// item 2, and "The failure"); the benchmark spec's fixed-order merge-states kernel.
+// item 2, and "The failure"): the splits' partial states are combined afterwards, here in
+// one fixed order per row.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>

@@ -1,13 +1,15 @@
 // Causal GQA prefill attention over a paged KV cache, gfx950 (CDNA4), wave64.
 //
-// One workgroup = one (q tile, KV split, kv head). Each wave owns 32 packed rows as two 16-row
-// MFMA column blocks; 8 waves (two per SIMD, 256-row tiles) at head_dim 128, 4 waves (one per
-// SIMD, 128-row tiles) at head_dim 256. Per KV tile of BN keys (64 at head_dim 128, 32 at
-// head_dim 256; tiles start at absolute multiples of BN):
-//   gather   every thread loads 16-byte chunks of K and V rows through the page table into
-//            registers, PF tiles ahead, then stores them into two LDS stages (natural
+// A unit = one (q tile, KV split, kv head); a workgroup runs one unit, or in a persistent
+// launch a chain of units. Each wave owns 32 packed rows as two 16-row MFMA column blocks;
+// 8 waves (two per SIMD, 256-row tiles) at head_dim 128, 4 waves (one per SIMD, 128-row
+// tiles) at head_dim 256. Per KV tile of BN keys (64 at head_dim 128, 32 at head_dim 256;
+// tiles start at absolute multiples of BN):
+//   gather   16-byte chunks of K and V rows come through the page table straight into a ring
+//            of four K and four V LDS buffers by LDS-DMA, several tiles ahead (natural
 //            [key][d] layout, 16-byte chunks XOR-swizzled by key). Keys past kv_len or on an
-//            out-of-range page are zero-filled; fp8 E4M3 chunks are decoded to bf16 on the way.
+//            out-of-range page read zeros; fp8 E4M3 chunks go through registers and are
+//            decoded to bf16 on the way.
 //   QK^T     S^T[key, row] = K Q^T on v_mfma_f32_16x16x32_bf16, fp32 accumulation over
 //            head_dim in ascending 32-wide chunks: keys on M, 16 query rows on N, so a lane
 //            holds scores of a single query row (4 keys of every 16-key block).

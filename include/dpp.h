@@ -2,10 +2,11 @@
  * dpp.h -- C ABI of libdpp: batch-invariant causal GQA prefill attention over a paged KV
  * cache, for AMD Instinct MI355X (gfx950).
  *
- * The operation (north_star definition; causal placement from sglang PR #46351, "Fix"
- * section and the author's reply on tail alignment): for request r with qo_len query tokens
- * and kv_len cached-plus-new tokens, query row i of q head h attends to keys 0..p of kv head
- * h / (num_qo_heads / num_kv_heads), where p = kv_len - qo_len + i, and returns
+ * The operation (paged causal prefill attention, sglang PR #46351 page, "Motivation"; causal
+ * placement from the same page, "Fix" section and the author's reply on tail alignment): for
+ * request r with qo_len query tokens and kv_len cached-plus-new tokens, query row i of q head h
+ * attends to keys 0..p of kv head h / (num_qo_heads / num_kv_heads), where
+ * p = kv_len - qo_len + i, and returns
  *
  *     o[i, h, :]  = softmax_j( sm_scale * <q[i, h, :], k[j, :]> ) @ v[j, :]      (bf16)
  *     lse[i, h]   = log sum_j exp( sm_scale * <q[i, h, :], k[j, :]> )            (fp32, natural log)

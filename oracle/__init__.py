@@ -12,8 +12,9 @@ Two independent implementations live here:
 * :func:`dense_attention_np` -- numpy fp64 brute force on a dense (un-paged) K/V with an
   explicit boolean mask; used only on tiny inputs to pin the C code.
 
-Sources for what is computed: the benchmark spec definition softmax(QK^T/sqrt(d) + causal
-mask)V over pages; the right-aligned causal placement of a query block against its KV
+Sources for what is computed: causal scaled-dot-product attention softmax(QK^T/sqrt(d) +
+causal mask)V over a paged KV cache, the prefill operation of the sglang PR #46351 page
+(Motivation); the right-aligned causal placement of a query block against its KV
 segment (sglang PR #46351, "Fix" section, and the author's reply on tail alignment); fixed
 KV splits whose partial states are combined afterwards (model-serving-minefield issue #73,
 correction comment, "What the flag actually does in this build", item 2).

@@ -16,7 +16,8 @@
  *     lse       = m + log(sum_j exp(s_j - m))          (natural log)
  *
  * with K_r[j] read through the page table: page kv_indices[kv_indptr[r] + j / page_size],
- * slot j % page_size. Sources: north_star's "softmax(QK^T/sqrt(d) + causal mask)V over pages";
+ * slot j % page_size. Sources: causal scaled-dot-product attention over a paged KV cache, the
+ * prefill operation of the sglang PR #46351 page (Motivation);
  * the query-to-position alignment is the one the sglang PR #46351 page states in its Fix
  * section and in the author's reply on tail alignment (row i sits at i + kv_len - qo_len,
  * key j is masked when j exceeds that position).

@@ -31,16 +31,16 @@ def _check_pairs(cached_batch, o_c, l_c, full_batch, o_f, l_f, pairs, what):
         assert_bits_equal(l_c[ia], l_f[ib], f"{what} lse req {rc}")
 
 
-def test_config1_single_extend(oracle):
-    work = wl.config1_single_extend()
+def test_single_extend(oracle):
+    work = wl.single_extend()
     dev = Device(work)
     full, cached = work.batches["full"], work.batches["cached"]
     o_f, l_f = dev.run(full)
     o_c, l_c = dev.run(cached)
     for b, o, l, name in ((full, o_f, l_f, "full"), (cached, o_c, l_c, "cached")):
         ro, rl = oracle_rows(oracle, work, b)
-        assert_close_to_oracle(o, l, ro, rl, what=f"config1 {name}")
-    _check_pairs(cached, o_c, l_c, full, o_f, l_f, [(0, 0)], "config1")
+        assert_close_to_oracle(o, l, ro, rl, what=f"single extend {name}")
+    _check_pairs(cached, o_c, l_c, full, o_f, l_f, [(0, 0)], "single extend")
 
 
 RANDOM_CASES = [
@@ -76,85 +76,85 @@ def test_random_against_oracle(oracle, case):
 
 
 @pytest.mark.parametrize("layout", ["radix", "distinct"])
-def test_config2_extend_batch(oracle, layout):
-    work = wl.config2_extend_batch(layout=layout)
+def test_extend_batch(oracle, layout):
+    work = wl.extend_batch(layout=layout)
     dev = Device(work)
     cached, full = work.batches["cached"], work.batches["full"]
     o_c, l_c = dev.run(cached)
     ro, rl = oracle_rows(oracle, work, cached)
-    assert_close_to_oracle(o_c, l_c, ro, rl, what=f"config2 {layout}")
+    assert_close_to_oracle(o_c, l_c, ro, rl, what=f"extend batch {layout}")
     o_f, l_f = dev.run(full)
-    _check_pairs(cached, o_c, l_c, full, o_f, l_f, [(i, i) for i in range(16)], f"config2 {layout}")
+    _check_pairs(cached, o_c, l_c, full, o_f, l_f, [(i, i) for i in range(16)], f"extend batch {layout}")
     # each extend alone gives the same bits as inside the batch
     for i in (0, 7, 15):
         one = wl.sub_batch(cached, work.prompts, work.page_size, [i])
         o1, l1 = dev.run(one)
         a, b = int(cached.qo_indptr[i]), int(cached.qo_indptr[i + 1])
-        assert_bits_equal(o1, o_c[a:b], f"config2 request {i} alone vs batched")
-        assert_bits_equal(l1, l_c[a:b], f"config2 request {i} alone vs batched (lse)")
+        assert_bits_equal(o1, o_c[a:b], f"extend batch request {i} alone vs batched")
+        assert_bits_equal(l1, l_c[a:b], f"extend batch request {i} alone vs batched (lse)")
 
 
-def test_config3_cold_prefill(oracle):
-    work = wl.config3_cold_prefill()
+def test_cold_prefill(oracle):
+    work = wl.cold_prefill()
     dev = Device(work)
     full = work.batches["full"]
     o, l = dev.run(full)
     rows = sample_rows(full, 24, seed=3)
     ro, rl = oracle_rows(oracle, work, full, rows)
-    assert_close_to_oracle(o, l, ro, rl, rows=rows, what="config3 sampled rows")
+    assert_close_to_oracle(o, l, ro, rl, rows=rows, what="cold prefill sampled rows")
     for i in (0, 9):
         one = wl.sub_batch(full, work.prompts, work.page_size, [i])
         o1, l1 = dev.run(one)
         a, b = int(full.qo_indptr[i]), int(full.qo_indptr[i + 1])
-        assert_bits_equal(o1, o[a:b], f"config3 request {i} alone vs batch of 16")
-        assert_bits_equal(l1, l[a:b], f"config3 request {i} alone vs batch of 16 (lse)")
+        assert_bits_equal(o1, o[a:b], f"cold prefill request {i} alone vs batch of 16")
+        assert_bits_equal(l1, l[a:b], f"cold prefill request {i} alone vs batch of 16 (lse)")
 
 
-def test_config4_mixed_batch(oracle):
-    work = wl.config4_mixed()
+def test_mixed_batch(oracle):
+    work = wl.mixed_batch()
     dev = Device(work)
     mixed, full = work.batches["mixed"], work.batches["full"]
     o_m, l_m = dev.run(mixed)
     rows = np.concatenate([sample_rows(wl.sub_batch(mixed, work.prompts, 16, [0]), 40, seed=4),
                            np.arange(3700, mixed.num_q_tokens)])
     ro, rl = oracle_rows(oracle, work, mixed, rows)
-    assert_close_to_oracle(o_m, l_m, ro, rl, rows=rows, what="config4 mixed batch")
+    assert_close_to_oracle(o_m, l_m, ro, rl, rows=rows, what="mixed batch")
     o_f, l_f = dev.run(full)
-    _check_pairs(mixed, o_m, l_m, full, o_f, l_f, [(i + 1, i) for i in range(7)], "config4")
+    _check_pairs(mixed, o_m, l_m, full, o_f, l_f, [(i + 1, i) for i in range(7)], "mixed batch")
     # the full 3700-token request in the mixed batch equals itself alone
     one = wl.sub_batch(mixed, work.prompts, 16, [0])
     o1, l1 = dev.run(one)
-    assert_bits_equal(o1, o_m[:3700], "config4 full request alone vs mixed")
-    assert_bits_equal(l1, l_m[:3700], "config4 full request alone vs mixed (lse)")
+    assert_bits_equal(o1, o_m[:3700], "mixed batch: full request alone vs mixed")
+    assert_bits_equal(l1, l_m[:3700], "mixed batch: full request alone vs mixed (lse)")
 
 
 @pytest.fixture(scope="module")
-def config5():
-    return wl.config5_long_fp8()
+def long_fp8_work():
+    return wl.long_fp8()
 
 
-def test_config5_long_fp8_parity(oracle, config5):
-    work = config5
+def test_long_fp8_parity(oracle, long_fp8_work):
+    work = long_fp8_work
     dev = Device(work)
     for name in ("prefill_8192", "extend"):
         b = work.batches[name]
         o, l = dev.run(b, cap=256 << 20)
         rows = sample_rows(b, 6, seed=5)
         ro, rl = oracle_rows(oracle, work, b, rows)
-        assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"config5 {name}")
+        assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"long fp8 {name}")
 
 
-def test_config5_extend_matches_32k_prefill(config5):
-    work = config5
+def test_long_fp8_extend_matches_32k_prefill(long_fp8_work):
+    work = long_fp8_work
     dev = Device(work)
     ext, full = work.batches["extend"], work.batches["prefill_32768"]
     o_e, l_e = dev.run(ext, cap=256 << 20)
     o_f, l_f = dev.run(full, cap=256 << 20)
-    _check_pairs(ext, o_e, l_e, full, o_f, l_f, [(0, 0)], "config5 extend vs 32k prefill")
+    _check_pairs(ext, o_e, l_e, full, o_f, l_f, [(0, 0)], "long fp8 extend vs 32k prefill")
 
 
-def test_config5_workspace_cap_does_not_change_bits(config5):
-    work = config5
+def test_long_fp8_workspace_cap_does_not_change_bits(long_fp8_work):
+    work = long_fp8_work
     dev = Device(work)
     b = work.batches["prefill_8192"]
     p_small = dev.plan(b, cap=32 << 20)
@@ -164,5 +164,5 @@ def test_config5_workspace_cap_does_not_change_bits(config5):
     assert p_small.workspace_bytes <= 32 << 20
     o1, l1 = dev.run(b, plan=p_small)
     o2, l2 = dev.run(b, plan=p_big)
-    assert_bits_equal(o1, o2, "config5 8k: cap 32 MiB vs unbounded")
-    assert_bits_equal(l1, l2, "config5 8k: cap 32 MiB vs unbounded (lse)")
+    assert_bits_equal(o1, o2, "long fp8 8k: cap 32 MiB vs unbounded")
+    assert_bits_equal(l1, l2, "long fp8 8k: cap 32 MiB vs unbounded (lse)")

@@ -161,7 +161,7 @@ def test_closed_form_one_hot(oracle_lib):
 
 
 def test_invariant_cached_tail_equals_full_rows(oracle_lib):
-    work = wl.config1_single_extend()
+    work = wl.single_extend()
     full, cached = work.batches["full"], work.batches["cached"]
     o_f, l_f = oracle_lib.paged_prefill(**work.oracle_kwargs(full))
     o_c, l_c = oracle_lib.paged_prefill(**work.oracle_kwargs(cached))
@@ -217,7 +217,7 @@ def test_invariant_gqa_equals_replicated_mha(oracle_lib):
 
 def test_never_reads_unused_slots(oracle_lib):
     """Pools are NaN outside the used slots; outputs stay finite."""
-    work = wl.config4_mixed(tails=(1, 5))
+    work = wl.mixed_batch(tails=(1, 5))
     o, lse = oracle_lib.paged_prefill(**work.oracle_kwargs(work.batches["mixed"]),
                                       rows=[0, 1000, 3699, 3700, 3701, 3705])
     assert np.isfinite(o).all() and np.isfinite(lse).all()

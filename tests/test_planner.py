@@ -353,6 +353,6 @@ def test_workload_batches_plan(dpp):
     for specs in ([(1028, 1028)] * 16, [(1024 + t, t) for t in (1, 2, 3, 4)] * 4):
         p = _plan(dpp, _specs_batch(specs))
         assert p.info.num_prefill_items > 0
-    work = wl.config1_single_extend()
+    work = wl.single_extend()
     p = _plan(dpp, work.batches["cached"])
     assert p.info.total_q_rows == 3

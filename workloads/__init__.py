@@ -229,7 +229,7 @@ def _pool_pages(token_counts, page_size: int, factor: int = 2) -> int:
     return max(64, factor * need)
 
 
-# --------------------------------------------------------------------------- the five configs
+# --------------------------------------------------------------------------- the five workloads
 
 QWEN3_8B = dict(hq=32, hkv=8, d=128)
 QWEN3_4B = dict(hq=32, hkv=8, d=128)
@@ -244,7 +244,7 @@ def _new(name, shapes, page_size, kv_dtype, pool, prompts, batches, desc):
                     prompts=prompts, batches=batches, description=desc)
 
 
-def config1_single_extend(seed_base: int = 1000, page_size: int = 16) -> Workload:
+def single_extend(seed_base: int = 1000, page_size: int = 16) -> Workload:
     """One 67-token prompt: full prefill vs 64-token cached prefix + 3-token extend.
 
     The two batches place the prompt's KV in different, seed-shuffled pages.
@@ -262,7 +262,7 @@ def config1_single_extend(seed_base: int = 1000, page_size: int = 16) -> Workloa
                 "64-token cached prefix")
 
 
-def config2_extend_batch(seed_base: int = 2000, page_size: int = 16, batch: int = 16,
+def extend_batch(seed_base: int = 2000, page_size: int = 16, batch: int = 16,
                          prefix: int = 1024, layout: str = "radix") -> Workload:
     """16 requests behind one shared 1024-token prefix, each extending 1-4 tokens (uniform).
 
@@ -296,7 +296,7 @@ def config2_extend_batch(seed_base: int = 2000, page_size: int = 16, batch: int 
                 f"{prefix}-token prefix ({layout} page layout)")
 
 
-def config3_cold_prefill(seed_base: int = 3000, page_size: int = 16, batch: int = 16,
+def cold_prefill(seed_base: int = 3000, page_size: int = 16, batch: int = 16,
                          length: int = 1028) -> Workload:
     """16 distinct prompts x 1028 tokens, full causal prefill, no cache hits."""
     s = dict(QWEN3_8B)
@@ -310,7 +310,7 @@ def config3_cold_prefill(seed_base: int = 3000, page_size: int = 16, batch: int 
                 f"32/8/128 bf16, cold causal prefill of {batch} x {length} tokens")
 
 
-def config4_mixed(seed_base: int = 4000, page_size: int = 16, prefix: int = 3700,
+def mixed_batch(seed_base: int = 4000, page_size: int = 16, prefix: int = 3700,
                   tails=(1, 2, 4, 6, 37, 64, 300)) -> Workload:
     """One 3700-token full prefill plus 7 cached-prefix requests with uncached tails.
 
@@ -340,7 +340,7 @@ def config4_mixed(seed_base: int = 4000, page_size: int = 16, prefix: int = 3700
                 + ", ".join(map(str, tails)))
 
 
-def config5_long_fp8(seed_base: int = 5000, page_size: int = 16, lengths=(8192, 32768),
+def long_fp8(seed_base: int = 5000, page_size: int = 16, lengths=(8192, 32768),
                      extend: int = 1024) -> Workload:
     """24/4/256 with an fp8 E4M3 KV cache (N(0,1) x 32, dequant scale 1/32).
 
