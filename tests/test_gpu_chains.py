@@ -66,3 +66,23 @@ def test_chained_and_unchained_launches_agree():
         assert_bits_equal(outs[page][0], outs[16][0], f"page {page} vs page 16")
         assert_bits_equal(outs[page][1], outs[16][1], f"page {page} vs page 16 (lse)")
     assert np.isfinite(outs[16][0].float().numpy()).all()
+
+
+def test_chained_passes_under_a_workspace_cap():
+    """A cap small enough to cut the partial-holding tiles of a 9000-token prompt into several
+    passes: every pass is its own persistent launch over its own unit records (plus a merge);
+    the rows are bit-identical to the uncapped single pass."""
+    specs = [(9000, 900), (1300, 1300), (600, 200)]
+    work = wl.random_workload(795, hq=32, hkv=8, d=128, page_size=16, kv_dtype="bf16", specs=specs)
+    dev = Device(work)
+    batch = work.batches["batch"]
+    free = dev.plan(batch)
+    capped = dev.plan(batch, cap=6 << 20)
+    say(f"passes: uncapped {free.info.num_passes}, capped {capped.info.num_passes}")
+    assert free.info.num_passes == 1 and capped.info.num_passes > 1
+    header = __import__("dpp_header").parse(capped.header())
+    assert len(set(int(x) for x in header.units[:, 14])) == capped.info.num_passes
+    o1, l1 = dev.run(batch, plan=free)
+    o2, l2 = dev.run(batch, plan=capped)
+    assert_bits_equal(o2, o1, "capped vs uncapped")
+    assert_bits_equal(l2, l1, "capped vs uncapped (lse)")
