@@ -36,6 +36,7 @@
 // arithmetic.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <climits>
 #include <cstdint>
 #include <type_traits>
@@ -105,6 +106,14 @@ __device__ inline int chunk_off(int key, int c) {
 template <int ROW_BYTES>
 __device__ inline int chunk_off_v(int key, int c) {
   return key * ROW_BYTES + ((c ^ ((key & 7) << 1)) << 4);
+}
+
+// Same for a V tile of half-width rows (head_dim D/2, 128 bytes at D = 128): 32-byte unit u of
+// key row `key` sits at unit u ^ ((key / 2) % 4), so the 8 keys a half-wave's transposing read
+// touches (32 bytes each) land on 8 distinct 32-byte bank groups.
+template <int ROW_BYTES>
+__device__ inline int chunk_off_vh(int key, int c) {
+  return key * ROW_BYTES + ((c ^ (((key >> 1) & 3) << 1)) << 4);
 }
 
 // OCP E4M3 code -> fp32 (exact): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
@@ -222,18 +231,28 @@ __device__ inline void wait_vmcnt() {
 //                  hardware returns zeros past it)
 constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2;
 
-// NB: 16-row blocks per wave.
-template <int D, bool FP8, int NB, int MODE>
+// NB: 16-row blocks per wave. VH (narrow bf16 kernel only): the launch runs every unit on two
+// workgroups, one per half of head_dim in PV. Both compute the unit's scores and softmax from
+// all of K; each loads only its half of V's columns and writes its half of the output. Every
+// output element still accumulates the same MFMA sequence, so the bits are those of one
+// workgroup; the unit's bytes per workgroup drop to 3/4 and twice the workgroups stream them.
+template <int D, bool FP8, int NB, int MODE, bool VH>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
   using C = Geo<D, NB>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // Narrow bf16 kernel with eight waves: wave 0 computes scores and softmax, wave 4 (on the
   // same SIMD) the output, and waves 2, 3, 6, 7 issue the DMA loads.
   constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
+  static_assert(!VH || (kSpec && MODE != kPagesScalar), "head_dim halves: narrow bf16 kernel, vector addresses");
+  // V ring: rows of head_dim (or of half of it, VH) per tile
+  constexpr int VROW = VH ? C::ROW_BYTES / 2 : C::ROW_BYTES;
+  constexpr int VTILE = VH ? C::TILE_BYTES / 2 : C::TILE_BYTES;
+  constexpr int RING = C::NBUF * (C::TILE_BYTES + VTILE);
+  constexpr int VDB = VH ? C::DB / 2 : C::DB;  // PV head_dim blocks of this workgroup
   // Two-group schedule (see below): bf16 wide tiles with two waves per SIMD. Its launches may
   // be persistent (a chain of units per workgroup).
   constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
-  unsigned char* xb = smem + C::LDS_BYTES;  // exchange buffer (kSpec)
+  unsigned char* xb = smem + RING;  // exchange buffer (kSpec)
   // page-id tables after the ring: raw ids from kv_indices, 4 bytes an entry; a persistent
   // launch alternates between two (the next unit's ids load during the current unit)
   unsigned char* pt0 = xb + (kSpec ? C::XBYTES : 0);
@@ -258,10 +277,18 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     return lane < kItemWords ? r[lane] : 0;
   };
   int32_t rv;
+  int vh = 0;  // VH: the half of head_dim this workgroup's PV covers (uniform)
   if (chained) {
     rv = fetch_record(blockIdx.x);
   } else {
-    const int w = xcd_chunked(blockIdx.x, a.num_items * a.num_kv_heads);
+    // VH: the two workgroups of a unit are work indices 2u and 2u + 1, so that both usually
+    // fall in one XCD's range and share its L2 for K
+    const int nw = a.num_items * a.num_kv_heads;
+    int w = xcd_chunked(blockIdx.x, VH ? 2 * nw : nw);
+    if constexpr (VH) {
+      vh = w & 1;
+      w >>= 1;
+    }
     const int h = w / a.num_items;
     const int32_t* r = a.header + a.item_offset + (a.item_begin + (w - h * a.num_items)) * kItemWords;
     rv = lane < kItemWords ? r[lane] : 0;
@@ -433,6 +460,27 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     pg_rel[i] = MODE == kPagesPow2 ? (krow[i] >> page_shift) : 0;
     in_page[i] = MODE == kPagesPow2 ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
   }
+  // V chunks: the same as K's, or, VH, the chunks of this workgroup's half rows (8 key rows
+  // of 128 bytes per wave-wide load at D = 128)
+  constexpr int NCHV = VH ? NCHT / 2 : NCHT;
+  static_assert(FP8 || NCHV * IW * 1024 == VTILE, "the issuing waves cover a V tile");
+  int vrow[NCHV], vcolh[NCHV], vpg_rel[NCHV];
+  int64_t vin_page[NCHV];
+#pragma unroll
+  for (int i = 0; i < NCHV; ++i) {
+    if constexpr (VH) {
+      const int q = (i * IW + iw) * 64 + lane;
+      constexpr int HCH = C::CH / 2;
+      vrow[i] = q / HCH;
+      const int slot = q % HCH;
+      vcolh[i] = (vh * HCH + (slot ^ (((vrow[i] >> 1) & 3) << 1))) * 8 * kElem;  // chunk_off_vh(.) == 16 q
+    } else {
+      vrow[i] = krow[i];
+      vcolh[i] = vcol[i];
+    }
+    vpg_rel[i] = MODE == kPagesPow2 ? (vrow[i] >> page_shift) : 0;
+    vin_page[i] = MODE == kPagesPow2 ? (int64_t)(vrow[i] & (page_size - 1)) * token_bytes : 0;
+  }
   // scalar pages: byte offset of the lane's chunk from its load's first key row
   int voff_k[NCHT], voff_v[NCHT];
 #pragma unroll
@@ -440,14 +488,14 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     voff_k[i] = (int)((krow[i] % C::KPI) * token_bytes) + kcol[i];
     voff_v[i] = (int)((krow[i] % C::KPI) * token_bytes) + vcol[i];
   }
-  // source of chunk i of item tile t of one tensor
-  auto chunk_src = [&](const unsigned char* base, int col, int t, int i) -> const unsigned char* {
+  // source of a chunk (key row `row` of the tile, byte column `col`) of item tile t of one tensor
+  auto chunk_src = [&](const unsigned char* base, int col, int row, int t) -> const unsigned char* {
     const int kt = kt0 + min(max(t, 0), n_tiles - 1);
-    const int key = kt * C::BN + krow[i];
+    const int key = kt * C::BN + row;
     int64_t pid, inpg;
     if constexpr (MODE == kPagesPow2) {
-      pid = pg_lds[((kt * C::BN) >> page_shift) - key_lo_page + pg_rel[i]];
-      inpg = in_page[i];
+      pid = pg_lds[((kt * C::BN) >> page_shift) - key_lo_page + (row >> page_shift)];
+      inpg = (int64_t)(row & (page_size - 1)) * token_bytes;
     } else {
       const int kk = min(key, rq.kv_len - 1);
       const int pi = kk / page_size;
@@ -466,44 +514,54 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   // read in iteration t - 1.
   static_assert(C::NBUF == 4, "the schedule below assumes four buffers");
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the dynamic block
-  auto dma_tile = [&](bool v, int t) {
-    const uint32_t buf = lds0 + (uint32_t)(((v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES);
-    const unsigned char* base = v ? vbase : kbase;
-    if constexpr (MODE == kPagesScalar) {
-      // scalar pages are issued by issue_group_scalar
-    } else if constexpr (pow2_pages) {
+  // LDS byte offset of ring buffer t of K or V
+  auto kbuf_off = [&](int t) { return (t & (C::NBUF - 1)) * C::TILE_BYTES; };
+  auto vbuf_off = [&](int t) { return C::NBUF * C::TILE_BYTES + (t & (C::NBUF - 1)) * VTILE; };
+  // N chunks of tile t: key rows, page of the row within its tile, offset in the page, column
+  auto dma_chunks = [&](const unsigned char* base, uint32_t buf, int t, const auto& rows, const auto& pgr,
+                        const auto& inp, const auto& cols) {
+    constexpr int N = std::extent<std::remove_reference_t<decltype(rows)>>::value;
+    if constexpr (pow2_pages) {
       // all page ids first (one LDS round trip), then selects: no branch per chunk
       const bool tile_ok = t >= 0 && t < n_tiles;
       const int kt = kt0 + min(max(t, 0), n_tiles - 1);
       const int lim = tile_ok ? rq.kv_len - kt * C::BN : 0;  // key row r exists iff r < lim
       const int tp = ((kt * C::BN) >> page_shift) - key_lo_page;
-      int32_t pid[NCHT];
+      int32_t pid[N];
 #pragma unroll
-      for (int i = 0; i < NCHT; ++i) pid[i] = pg_lds[tp + pg_rel[i]];
+      for (int i = 0; i < N; ++i) pid[i] = pg_lds[tp + pgr[i]];
 #pragma unroll
-      for (int i = 0; i < NCHT; ++i) {
-        const bool ok = krow[i] < lim && pid[i] >= 0 && pid[i] < a.num_pages;
+      for (int i = 0; i < N; ++i) {
+        const bool ok = rows[i] < lim && pid[i] >= 0 && pid[i] < a.num_pages;
         const uint64_t off = (uint64_t)(uint32_t)(ok ? pid[i] : 0) * (uint64_t)page_bytes +
-                             (uint64_t)in_page[i] + (uint64_t)(v ? vcol[i] : kcol[i]);
+                             (uint64_t)inp[i] + (uint64_t)cols[i];
         dma16(ok ? base + off : zero16, buf + (uint32_t)((i * IW + iw) * 1024));
       }
     } else {
 #pragma unroll
-      for (int i = 0; i < NCHT; ++i)
-        dma16(chunk_src(base, v ? vcol[i] : kcol[i], t, i), buf + (uint32_t)((i * IW + iw) * 1024));
+      for (int i = 0; i < N; ++i) dma16(chunk_src(base, cols[i], rows[i], t), buf + (uint32_t)((i * IW + iw) * 1024));
+    }
+  };
+  auto dma_tile = [&](bool v, int t) {
+    if constexpr (MODE == kPagesScalar) {
+      // scalar pages are issued by issue_group_scalar
+    } else if (v) {
+      dma_chunks(vbase, lds0 + (uint32_t)vbuf_off(t), t, vrow, vpg_rel, vin_page, vcolh);
+    } else {
+      dma_chunks(kbase, lds0 + (uint32_t)kbuf_off(t), t, krow, pg_rel, in_page, kcol);
     }
   };
   u32x2 kreg[C::NCH], vreg[C::NCH];  // fp8 staging of one load group
   auto fp8_load = [&](int tk, int tv) {
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
-      kreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(kbase, kcol[i], tk, i));
-      vreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(vbase, vcol[i], tv, i));
+      kreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(kbase, kcol[i], krow[i], tk));
+      vreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(vbase, vcol[i], krow[i], tv));
     }
   };
   auto fp8_store = [&](int tk, int tv) {
-    unsigned char* kb = smem + (tk & (C::NBUF - 1)) * C::TILE_BYTES;
-    unsigned char* vb = smem + (C::NBUF + (tv & (C::NBUF - 1))) * C::TILE_BYTES;
+    unsigned char* kb = smem + kbuf_off(tk);
+    unsigned char* vb = smem + vbuf_off(tv);
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
       *reinterpret_cast<u32x4*>(kb + lds_k[i]) = dequant8(kreg[i], a.k_scale);
@@ -569,19 +627,19 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     if constexpr (MODE == kPagesScalar) issue_group_scalar(t);
     else issue_group(t);
   };
-  constexpr int kGroupLoads = kLoads;
+  constexpr int kGroupLoads = MODE == kPagesScalar ? kLoads : NCHT + NCHV;  // one thread's loads of a group
 
   // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
   float m_sc[NB], l_sum[NB];  // reference max (scaled, base 2) and running sum per row
-  f32x4 acc[C::DB][NB];
+  f32x4 acc[VDB][NB];
   auto reset_state = [&]() {
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       m_sc[nb] = -INFINITY;
       l_sum[nb] = 0.f;
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int db = 0; db < VDB; ++db) acc[db][nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   };
   reset_state();
@@ -628,11 +686,11 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l_sum[nb]);
       if (mine && p < kSplitTokens) {
         const int64_t orow = out_row(lr);
-        if (lg == 0) lse_out[orow] = lse2 * kLn2;
+        if (lg == 0 && vh == 0) lse_out[orow] = lse2 * kLn2;
         if constexpr (!kPP) {
-          DPP_GLOBAL uint16_t* op = o_out + orow * D + 4 * lg;
+          DPP_GLOBAL uint16_t* op = o_out + orow * D + vh * (D / 2) + 4 * lg;
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db)
+          for (int db = 0; db < VDB; ++db)
             *reinterpret_cast<DPP_GLOBAL u32x2*>(op + db * 16) =
                 u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
                       pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
@@ -640,16 +698,16 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       } else if (mine) {
         // a row reaching past the first split: its fp32 partial, straight from the MFMA layout
         const int64_t slot = partial_slot(e.slot_base, e.tile_splits, e.kv_head, e.split, lr, C::PLAN_BM);
-        DPP_GLOBAL float* pp = part_o_out + slot * D + 4 * lg;
+        DPP_GLOBAL float* pp = part_o_out + slot * D + vh * (D / 2) + 4 * lg;
 #pragma unroll
-        for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < VDB; ++db)
           *reinterpret_cast<DPP_GLOBAL f32x4*>(pp + db * 16) =
               f32x4{acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l, acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l};
-        if (lg == 0) part_lse_out[slot] = lse2;
+        if (lg == 0 && vh == 0) part_lse_out[slot] = lse2;
       }
       if constexpr (kPP) {
 #pragma unroll
-      for (int sp = 0; sp < C::DB / 4; ++sp) {  // head_dim [64 sp, +64)
+      for (int sp = 0; sp < VDB / 4; ++sp) {  // head_dim [64 sp, +64)
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int db = 4 * sp + k;
@@ -758,7 +816,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       if constexpr (kRescale) {
         if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
 #pragma unroll
-          for (int db = 0; db < C::DB; ++db) acc[db][nb] *= alpha[nb];
+          for (int db = 0; db < VDB; ++db) acc[db][nb] *= alpha[nb];
         }
       }
       // P^T as the PV B operand: k = 8lg + i is key 32kc + 16(i/4) + 4lg + i%4
@@ -779,18 +837,20 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   // V[32kc + 16h + 4lg + j][16db + li] for j = 0..3 -- the A operand's k = 8lg + 4h + j.
   auto no_hook = [](int) {};
   auto pv_acc = [&](const bf16x8 (&pb)[C::KC][NB], int t, auto&& hook) {
-    const unsigned char* v_lds = smem + (C::NBUF + (t & (C::NBUF - 1))) * C::TILE_BYTES;
+    const unsigned char* v_lds = smem + vbuf_off(t);
     // step st = (kc, db) with kc outer: every acc[db][nb] accumulates key chunks kc = 0, 1,
-    // ... in that order; each step's V^T operand is read kAhead steps ahead
-    constexpr int kS = C::KC * C::DB;
+    // ... in that order; each step's V^T operand is read kAhead steps ahead. With VH, db
+    // counts the blocks of this workgroup's half of head_dim.
+    constexpr int kS = C::KC * VDB;
     auto read_v = [&](int st) {
-      const int kc = st / C::DB, db = st % C::DB;
+      const int kc = st / VDB, db = st % VDB;
       s16x4 hv[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
         const int e = db * 16 + 4 * (li & 3);
-        const unsigned char* addr = v_lds + chunk_off_v<C::ROW_BYTES>(key, e >> 3) + (e & 7) * 2;
+        const int off = VH ? chunk_off_vh<VROW>(key, e >> 3) : chunk_off_v<VROW>(key, e >> 3);
+        const unsigned char* addr = v_lds + off + (e & 7) * 2;
         hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
       }
       return __builtin_bit_cast(bf16x8, __builtin_shufflevector(hv[0], hv[1], 0, 1, 2, 3, 4, 5, 6, 7));
@@ -801,7 +861,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 #pragma unroll
     for (int st = 0; st < kS; ++st) {
       if (st + kAhead < kS) va[(st + kAhead) % (kAhead + 1)] = read_v(st + kAhead);
-      const int kc = st / C::DB, db = st % C::DB;
+      const int kc = st / VDB, db = st % VDB;
 #pragma unroll
       for (int nb = 0; nb < NB; ++nb) acc[db][nb] = mfma16(va[st % (kAhead + 1)], pb[kc][nb], acc[db][nb]);
       hook(st);  // work to overlap with this step's MFMAs
@@ -862,7 +922,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       for (int kc = 0; kc < C::KC; ++kc) pb[kc][0] = *reinterpret_cast<const bf16x8*>(slot + (kc * 64 + lane) * 16);
       const float al = *reinterpret_cast<const float*>(slot + 64 * C::KC * 16 + lane * 4);
 #pragma unroll
-      for (int db = 0; db < C::DB; ++db) acc[db][0] *= al;
+      for (int db = 0; db < VDB; ++db) acc[db][0] *= al;
       pv_acc(pb, t, no_hook);
     };
     auto spec_iter = [&](int t, f32x4 (&sc)[C::KB][NB], f32x4 (&sn)[C::KB][NB]) {
@@ -1064,29 +1124,45 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   }
 }
 
-template <int D, bool FP8, int NB, int MODE>
+template <int D, bool FP8, int NB, int MODE, bool VH = false>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   using C = Geo<D, NB>;
+  constexpr int kRing = C::NBUF * (C::TILE_BYTES + (VH ? C::TILE_BYTES / 2 : C::TILE_BYTES));
   // page-id tables (4 bytes an entry): a unit's pages plus one tile's worth of slack for the
   // last tile's lookups past kv_len (their chunks read the zero chunk); two in a persistent
   // launch
   constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
   const size_t pt_bytes = (size_t)page_table_bytes(a.page_slots, D);
   constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
-  const size_t lds = (size_t)C::LDS_BYTES + (kSpec ? C::XBYTES : 0) + (a.chain_offset >= 0 ? 2 : 1) * pt_bytes +
+  const size_t lds = (size_t)kRing + (kSpec ? C::XBYTES : 0) + (a.chain_offset >= 0 ? 2 : 1) * pt_bytes +
                      (kPP ? (size_t)kOutStageBytes : 0);
   if (lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE, VH>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
   }
-  dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains : a.num_items * a.num_kv_heads));
+  if (VH && a.chain_offset >= 0) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains : (VH ? 2 : 1) * a.num_items * a.num_kv_heads));
   if (a.chain_offset >= 0 && !chained_launch(D, FP8, NB == 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE>), grid, dim3(C::THREADS), lds, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE, VH>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
+}
+
+// Compute units of the current device (queried once per device).
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return kPersistentBlocks;
+  int v = cached[dev].load(std::memory_order_relaxed);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = kPersistentBlocks;
+    cached[dev].store(v, std::memory_order_relaxed);
+  }
+  return v;
 }
 
 template <int D, int NB>
@@ -1101,6 +1177,14 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   // suit them. The wide kernel's waves are busy with the softmax: scalar descriptors.
   if constexpr (NB > 1) {
     if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
+  } else if constexpr (waves_for(D) == 8) {
+    // A narrow launch of at most one unit per two compute units splits head_dim in PV over
+    // two workgroups per unit (same bits; a unit streams K/V at the rate one CU sustains, so
+    // the otherwise idle CUs take a quarter of its bytes each).
+    if (2 * a.num_items * a.num_kv_heads <= compute_units()) {
+      return pow2 && P <= block_n_for(D) ? launch_one<D, false, NB, kPagesPow2, true>(a, stream)
+                                         : launch_one<D, false, NB, kPagesGeneral, true>(a, stream);
+    }
   }
   return pow2 && P <= block_n_for(D) ? launch_one<D, false, NB, kPagesPow2>(a, stream)
                                      : launch_one<D, false, NB, kPagesGeneral>(a, stream);
