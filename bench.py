@@ -13,6 +13,9 @@ value     extend KV GB/s: 16 requests, each extending 1-4 tokens behind a 1024-t
           of its prefix pages and 8 such pools are rotated across steps (> 512 MB), so the
           256 MB Infinity Cache cannot serve the KV: logical KV bytes / step time.
 prefill   cold 16 x 1028-token causal prefill, same shapes: causal FLOPs / step time.
+decode    8 one-token decodes over 8k-128k keys each (same shapes, 2-32 KV splits a row, the
+          split partials merged): logical KV bytes / step time (1.4 GB of KV, far past the
+          Infinity Cache).
 roofline  the extend kernel against HBM (8 TB/s); prefill's own against bf16 MFMA peak.
 cpu_baseline  the fp64 CPU oracle on the same extend batch, repeated for ~10 s.
 """
@@ -172,7 +175,8 @@ def main() -> int:
     ap.add_argument("--cpu-budget-s", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only", choices=["extend", "prefill", "copy"], default=None,
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--only", choices=["extend", "prefill", "decode", "copy"], default=None,
                     help="run one leg only and print its timing (for profiler runs)")
     args = ap.parse_args()
 
@@ -262,6 +266,23 @@ def main() -> int:
                                  plan_us=pr.plan_us, items=pr.plan.info.num_prefill_items)
         del pr
 
+    # ---------------------------------------------------------------- long-KV decode
+    if args.only in (None, "decode") and not args.no_decode:
+        log("building long-KV decode workload")
+        work_d = wl.decode_batch(full_prompts=0)
+        bd = work_d.batches["decode"]
+        dr = Runner(work_d, bd, replicas=1)
+        ms_d, _ = dr.timed(max(10, args.steps // 4), max(5, args.warmup // 4))
+        if args.only == "decode":
+            log(f"decode: {ms_d * 1e3:.2f} us/step")
+            return 0
+        nb = kv_bytes(bd, hkv, d, 2)
+        result["decode"] = dict(ms=ms_d, kv_bytes=nb, gbps=nb / (ms_d * 1e-3) / 1e9,
+                                items=dr.plan.info.num_prefill_items,
+                                merges=dr.plan.info.num_merge_items,
+                                workspace=dr.plan.info.workspace_bytes)
+        del dr
+
     ext = result["extend"]
     traffic = traffic_from_profile(ext["alg_bytes"])
     line = {
@@ -304,6 +325,17 @@ def main() -> int:
                            "roofline": {"bound": "mfma", "achieved": round(p["tflops"], 2),
                                         "peak": BF16_MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                                         "frac": round(p["tflops"] / BF16_MFMA_PEAK_TFLOPS, 4)}}
+    if "decode" in result:
+        dd = result["decode"]
+        line["decode"] = {"workload": "long-KV decode, 8 requests x 1 token over " +
+                                      "/".join(str(n) for n in wl.DECODE_KV_LENS) +
+                                      " keys, 32/8/128 bf16, page 16",
+                          "kv_gbps": round(dd["gbps"], 2), "us_per_step": round(dd["ms"] * 1e3, 2),
+                          "kv_bytes_per_step": dd["kv_bytes"], "work_items": dd["items"],
+                          "merge_items": dd["merges"], "workspace_bytes": dd["workspace"],
+                          "roofline": {"bound": "hbm", "achieved": round(dd["gbps"], 2),
+                                       "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                                       "frac": round(dd["gbps"] / HBM_PEAK_GBPS, 4)}}
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(ext["work"], ext["batch"], args.cpu_budget_s)

@@ -32,13 +32,14 @@ FP8_DATA_SCALE = 32.0   # N(0,1) values are multiplied by this before E4M3 encod
 
 @dataclass
 class Prompt:
-    q: torch.Tensor  # bf16 [L, Hq, d]
+    q: torch.Tensor  # bf16 [L - q_from, Hq, d]: queries of tokens q_from .. L-1
     k: torch.Tensor  # storage dtype [L, Hkv, d] (bf16, or uint8 E4M3 codes)
     v: torch.Tensor
+    q_from: int = 0  # first token with a query (long decode prompts keep only their last ones)
 
     @property
     def length(self) -> int:
-        return int(self.q.shape[0])
+        return int(self.k.shape[0])
 
 
 @dataclass
@@ -111,17 +112,21 @@ def _to_storage(x: torch.Tensor, kv_dtype: str) -> torch.Tensor:
     raise ValueError(kv_dtype)
 
 
-def draw_prompt(length: int, hq: int, hkv: int, d: int, kv_dtype: str, seed: int) -> Prompt:
-    """q, k, v ~ N(0, 1) (k, v scaled by 32 before E4M3 encoding when kv_dtype is fp8)."""
-    q = _randn((length, hq, d), seed * 7 + 1).to(torch.bfloat16)
+def draw_prompt(length: int, hq: int, hkv: int, d: int, kv_dtype: str, seed: int,
+                q_from: int = 0) -> Prompt:
+    """q, k, v ~ N(0, 1) (k, v scaled by 32 before E4M3 encoding when kv_dtype is fp8).
+
+    Queries are drawn for tokens q_from .. length-1 only."""
+    q = _randn((length - q_from, hq, d), seed * 7 + 1).to(torch.bfloat16)
     k = _to_storage(_randn((length, hkv, d), seed * 7 + 2), kv_dtype)
     v = _to_storage(_randn((length, hkv, d), seed * 7 + 3), kv_dtype)
-    return Prompt(q, k, v)
+    return Prompt(q, k, v, q_from)
 
 
 def extend_prompt(base: Prompt, extra: int, hq: int, hkv: int, d: int, kv_dtype: str,
                   seed: int) -> Prompt:
     """A prompt whose first tokens are ``base`` (a shared prefix) followed by fresh tokens."""
+    assert base.q_from == 0
     tail = draw_prompt(extra, hq, hkv, d, kv_dtype, seed)
     return Prompt(torch.cat([base.q, tail.q]), torch.cat([base.k, tail.k]),
                   torch.cat([base.v, tail.v]))
@@ -190,7 +195,9 @@ def make_batch(requests: list, prompts: list, page_size: int) -> PagedBatch:
         kvp.append(kvp[-1] + len(r.pages))
         idx.extend(r.pages)
         last.append(r.kv_len - (len(r.pages) - 1) * page_size if r.pages else 0)
-        qs.append(prompts[r.prompt].q[r.kv_len - r.qo_len:r.kv_len])
+        p = prompts[r.prompt]
+        assert r.kv_len - r.qo_len >= p.q_from, "a query row the prompt does not hold"
+        qs.append(p.q[r.kv_len - r.qo_len - p.q_from:r.kv_len - p.q_from])
     hq, d = prompts[0].q.shape[1:]
     q = torch.cat(qs) if qs else torch.zeros((0, hq, d), dtype=torch.bfloat16)
     return PagedBatch(requests=list(requests),
@@ -367,6 +374,34 @@ def long_fp8(seed_base: int = 5000, page_size: int = 16, lengths=(8192, 32768),
     return _new("long_fp8_24x4x256", s, page_size, "fp8_e4m3", pool, prompts, batches,
                 "24/4/256, fp8 E4M3 KV: prefills of " + ", ".join(map(str, lengths))
                 + f" tokens and a {extend}-token extend behind a {prefix}-token prefix")
+
+
+DECODE_KV_LENS = (8192, 8999, 16384, 24001, 32768, 50000, 65536, 131072)
+
+
+def decode_batch(seed_base: int = 6000, page_size: int = 16, kv_lens=DECODE_KV_LENS,
+                 full_prompts: int = 2) -> Workload:
+    """Long-KV decode: one new token per request over 8k-128k cached tokens (32/8/128 bf16).
+
+    Every request owns its pages (distinct prompts). The lengths sit on and between the
+    4096-token split boundaries, so rows span 2 to 32 splits. Batches: "decode" (the one-row
+    requests) and "full" (the full prefill of the first ``full_prompts`` prompts, placed in
+    other pages, whose last rows are the same computations as those decode rows). Only those
+    prompts carry queries for every token; the others hold their last token's only.
+    """
+    s = dict(QWEN3_8B)
+    prompts = [draw_prompt(L, s["hq"], s["hkv"], s["d"], "bf16", seed_base + 1 + 10 * i,
+                           q_from=0 if i < full_prompts else L - 1)
+               for i, L in enumerate(kv_lens)]
+    lens = list(kv_lens)
+    pool = PagePool(_pool_pages(lens + lens[:full_prompts], page_size), page_size, s["hkv"],
+                    s["d"], "bf16", seed_base + 4)
+    dec = [Request(i, L, 1, pool.place(prompts[i], L)) for i, L in enumerate(lens)]
+    full = [Request(i, L, L, pool.place(prompts[i], L)) for i, L in enumerate(lens[:full_prompts])]
+    return _new("decode_8x1_over_8k-128k", s, page_size, "bf16", pool, prompts,
+                {"decode": make_batch(dec, prompts, page_size),
+                 "full": make_batch(full, prompts, page_size)},
+                "32/8/128 bf16: 8 one-token decodes over " + ", ".join(map(str, lens)) + " keys")
 
 
 def random_workload(seed: int, *, hq: int, hkv: int, d: int, page_size: int, kv_dtype: str,
