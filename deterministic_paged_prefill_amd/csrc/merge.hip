@@ -36,27 +36,45 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 
 // Combine S partials of one row for 4 consecutive columns. lse2_at(s) gives the split's
 // base-2 lse (-inf = empty partial, skipped), o_at(s) its 4 columns. Returns the combined
-// columns and writes the combined base-2 lse (or -inf) to *lse2_out.
+// columns and writes the combined base-2 lse (or -inf) to *lse2_out. The partials are loaded
+// kBatch splits at a time, all loads of a batch in flight together; the arithmetic still
+// takes the splits one by one in ascending order.
+constexpr int kBatch = 8;
 template <class LseAt, class OAt>
 __device__ inline f32x4 merge4(int S, LseAt lse2_at, OAt o_at, float* lse2_out) {
   float M = -INFINITY;
-  for (int s = 0; s < S; ++s) M = fmaxf(M, lse2_at(s));
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float l[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) l[u] = s0 + u < S ? lse2_at(s0 + u) : -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) M = fmaxf(M, l[u]);
+  }
   if (M == -INFINITY) {
     *lse2_out = -INFINITY;
     return f32x4{0.f, 0.f, 0.f, 0.f};
   }
   f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
-  for (int s = 0; s < S; ++s) {
-    const float l2 = lse2_at(s);
-    if (l2 == -INFINITY) continue;
-    const float w = (l2 == M) ? 1.f : __builtin_amdgcn_exp2f(l2 - M);
-    const f32x4 os = o_at(s);
-    num[0] = __builtin_fmaf(w, os[0], num[0]);
-    num[1] = __builtin_fmaf(w, os[1], num[1]);
-    num[2] = __builtin_fmaf(w, os[2], num[2]);
-    num[3] = __builtin_fmaf(w, os[3], num[3]);
-    den = den + w;
+  for (int s0 = 0; s0 < S; s0 += kBatch) {
+    float l[kBatch];
+    f32x4 os[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool in = s0 + u < S;
+      l[u] = in ? lse2_at(s0 + u) : -INFINITY;
+      os[u] = in ? o_at(s0 + u) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (l[u] == -INFINITY) continue;  // empty partial, or past the last split
+      const float w = (l[u] == M) ? 1.f : __builtin_amdgcn_exp2f(l[u] - M);
+      num[0] = __builtin_fmaf(w, os[u][0], num[0]);
+      num[1] = __builtin_fmaf(w, os[u][1], num[1]);
+      num[2] = __builtin_fmaf(w, os[u][2], num[2]);
+      num[3] = __builtin_fmaf(w, os[u][3], num[3]);
+      den = den + w;
+    }
   }
   const float inv = 1.f / den;
   *lse2_out = M + __builtin_amdgcn_logf(den);
