@@ -8,6 +8,9 @@ device memory and the current stream.
     p = dpp.plan(32, 8, 128, 16, qo_indptr, kv_indptr, kv_last_page_len)   # host int32 arrays
     o, lse = p.run(q, k_pool, v_pool, kv_indices)                           # device tensors
 
+Ragged (contiguous) KV: ``page_size=0``, ``kv_indptr`` in tokens, no ``kv_last_page_len``;
+``run(q, k, v)`` with k, v ``[tokens, Hkv, D]`` and no page list.
+
 Importing the package does not load the library; the first call does, and raises
 :class:`LibraryNotBuilt` if ``libdpp.so`` is missing (build it with
 ``python -m deterministic_paged_prefill_amd.build``). There is no CPU fallback.
@@ -184,7 +187,7 @@ class Plan:
                                          _stream_handle(stream)))
         self._ran = True
 
-    def run(self, q, k_pool, v_pool, kv_indices, out=None, lse=None, workspace=None,
+    def run(self, q, k_pool, v_pool, kv_indices=None, out=None, lse=None, workspace=None,
             stream=None, reuse_upload: bool = False):
         """Attention of the planned batch. Returns (o bf16 [rows, Hq, D], lse fp32 [rows, Hq]).
 
@@ -196,10 +199,12 @@ class Plan:
         if q.dtype != torch.bfloat16 or q.dim() != 3 or tuple(q.shape[1:]) != (c.num_qo_heads, c.head_dim):
             raise ValueError(f"q must be bf16 [rows, {c.num_qo_heads}, {c.head_dim}], got "
                              f"{q.dtype} {tuple(q.shape)}")
-        want = (c.page_size, c.num_kv_heads, c.head_dim)
+        ragged = c.page_size == 0
+        want = (c.num_kv_heads, c.head_dim) if ragged else (c.page_size, c.num_kv_heads, c.head_dim)
         for name, pool in (("k_pool", k_pool), ("v_pool", v_pool)):
-            if pool.dim() != 4 or tuple(pool.shape[1:]) != want:
-                raise ValueError(f"{name} must be [num_pages, {want[0]}, {want[1]}, {want[2]}], "
+            if pool.dim() != len(want) + 1 or tuple(pool.shape[1:]) != want:
+                lead = "tokens" if ragged else "num_pages"
+                raise ValueError(f"{name} must be [{lead}, {', '.join(map(str, want))}], "
                                  f"got {tuple(pool.shape)}")
             ok = (pool.dtype == torch.bfloat16) if c.kv_dtype == 0 else \
                 (pool.dtype in (torch.uint8, torch.float8_e4m3fn))
@@ -209,7 +214,11 @@ class Plan:
                 raise ValueError(f"{name} must be a contiguous device tensor")
         if k_pool.shape[0] != v_pool.shape[0]:
             raise ValueError("k_pool and v_pool must have the same number of pages")
-        if kv_indices.dtype != torch.int32 or not kv_indices.is_cuda or not kv_indices.is_contiguous():
+        if ragged:
+            if kv_indices is not None:
+                raise ValueError("ragged KV takes no kv_indices")
+        elif kv_indices is None or kv_indices.dtype != torch.int32 or not kv_indices.is_cuda or \
+                not kv_indices.is_contiguous():
             raise ValueError("kv_indices must be a contiguous int32 device tensor")
         if not q.is_cuda or not q.is_contiguous():
             raise ValueError("q must be a contiguous device tensor")
@@ -226,7 +235,7 @@ class Plan:
                 raise ValueError("reuse_upload needs the workspace the plan was uploaded to")
             workspace = self.new_workspace(q.device)
         status = library().dpp_run(self._h, q.data_ptr(), rows, k_pool.data_ptr(), v_pool.data_ptr(),
-                                   k_pool.shape[0], kv_indices.data_ptr(), out.data_ptr(),
+                                   k_pool.shape[0], None if ragged else kv_indices.data_ptr(), out.data_ptr(),
                                    lse.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(),
                                    RUN_REUSE_UPLOAD if reuse_upload else 0,
@@ -251,14 +260,19 @@ class Plan:
 
 
 def plan(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, qo_indptr,
-         kv_indptr, kv_last_page_len, *, kv_dtype: str = "bf16", sm_scale: float | None = None,
+         kv_indptr, kv_last_page_len=None, *, kv_dtype: str = "bf16", sm_scale: float | None = None,
          k_scale: float = 1.0, v_scale: float = 1.0,
          workspace_cap: int = DEFAULT_WORKSPACE_CAP) -> Plan:
     """Plan one batch from host copies of its index arrays (no GPU work)."""
     if kv_dtype not in KV_DTYPES:
         raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
-    qo, kvp, last = _i32(qo_indptr), _i32(kv_indptr), _i32(kv_last_page_len)
+    qo, kvp = _i32(qo_indptr), _i32(kv_indptr)
     batch = len(qo) - 1
+    if kv_last_page_len is None:
+        if page_size != 0:
+            raise ValueError("a paged layout needs kv_last_page_len")
+        kv_last_page_len = np.zeros(max(batch, 0), dtype=np.int32)  # ignored for ragged KV
+    last = _i32(kv_last_page_len)
     if batch < 0 or len(kvp) != batch + 1 or len(last) != batch:
         raise ValueError("need qo_indptr[B+1], kv_indptr[B+1], kv_last_page_len[B]")
     cfg = _Config(num_qo_heads, num_kv_heads, head_dim, page_size, KV_DTYPES[kv_dtype],

@@ -5,6 +5,7 @@
 // planning itself stays HIP-free).
 #include <hip/hip_runtime.h>
 
+#include <cstddef>
 #include <cstring>
 #include <string>
 
@@ -82,10 +83,15 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   if (st != DPP_OK) return st;
   if (plan->total_q_rows > 0 && (!q || !o || !lse))
     return fail(DPP_ERR_INVALID, "dpp_run: null q, o or lse");
-  if (plan->num_items > 0 && (!k_pool || !v_pool || !kv_indices))
+  if (plan->num_items > 0 && (!k_pool || !v_pool || (!kv_indices && !plan->ragged)))
     return fail(DPP_ERR_INVALID, "dpp_run: null k_pool, v_pool or kv_indices");
+  // ragged KV: num_pages counts the token rows of k_pool / v_pool, which every request's
+  // [kv_indptr[r], kv_indptr[r+1]) must lie within (the kernels do not check it per key)
+  if (plan->ragged && plan->total_kv_tokens > num_pages)
+    return fail(DPP_ERR_SHAPE, "ragged KV: kv_indptr[-1] = " + std::to_string(plan->total_kv_tokens) +
+                                   " tokens but k/v hold " + std::to_string(num_pages));
   if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(lse, 4) || !aligned(kv_indices, 4))
+      !aligned(lse, 4) || (!plan->ragged && !aligned(kv_indices, 4)))
     return fail(DPP_ERR_INVALID, "dpp_run: q/o/k_pool/v_pool must be 16-byte aligned");
   hipStream_t stream = (hipStream_t)stream_ptr;
   if (plan->num_items == 0) return DPP_OK;
@@ -100,7 +106,9 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
-  a.kv_indices = kv_indices;
+  // ragged: every unit's one page id (0) comes from the work list's zero chunk
+  a.kv_indices = plan->ragged ? (const int32_t*)workspace + offsetof(HeaderPreamble, zero_chunk) / 4 : kv_indices;
+  a.ragged = plan->ragged ? 1 : 0;
   a.o = o;
   a.lse = lse;
   a.header = (const int32_t*)workspace;
@@ -111,7 +119,7 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   a.num_qo_heads = plan->cfg.num_qo_heads;
   a.num_kv_heads = plan->cfg.num_kv_heads;
   a.group = plan->group;
-  a.page_size = plan->cfg.page_size;
+  a.page_size = plan->ragged ? kRaggedPage : plan->cfg.page_size;
   a.page_slots = plan->page_slots;
   a.item_offset = plan->item_offset;
   a.scale_log2 = plan->scale_log2;

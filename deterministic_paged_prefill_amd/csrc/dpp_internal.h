@@ -73,6 +73,9 @@ DPP_HOST_DEVICE constexpr bool chained_launch(int head_dim, bool fp8, bool narro
 }
 
 constexpr int kSplitTokens = 4096;
+// Ragged (contiguous) KV: one virtual page per request, this many tokens long, whose id is 0
+// (read from the work list's zero chunk) and whose base is the request's first token.
+constexpr int kRaggedPage = 1 << 30;
 static_assert(kSplitTokens % 64 == 0 && kSplitTokens % 32 == 0, "splits must be whole KV tiles");
 
 constexpr uint32_t kHeaderMagic = 0x44505031u;  // "DPP1"
@@ -173,8 +176,10 @@ struct PrefillArgs {
   int32_t num_qo_heads;
   int32_t num_kv_heads;
   int32_t group;
-  int32_t page_size;
+  int32_t page_size;        // kRaggedPage for a ragged (contiguous) KV layout
   int32_t page_slots;       // entries of one unit's page-id table in LDS
+  int32_t ragged;           // 1: K/V are [tokens, Hkv, D]; a request's page_start is its first
+                            // token and its keys sit on one virtual page with id 0
   float scale_log2;         // sm_scale * log2(e), rounded once to fp32
   float k_scale;
   float v_scale;

@@ -140,7 +140,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   if (out_plan) *out_plan = nullptr;
   if (!cfg || !out_plan) return fail(DPP_ERR_INVALID, "dpp_plan_create: null cfg or out_plan");
   if (batch_size < 0) return fail(DPP_ERR_INVALID, "dpp_plan_create: negative batch_size");
-  if (!qo_indptr || !kv_indptr || (batch_size > 0 && !last_page_len))
+  const bool ragged = cfg && cfg->page_size == 0;
+  if (!qo_indptr || !kv_indptr || (batch_size > 0 && !last_page_len && !ragged))
     return fail(DPP_ERR_INVALID, "dpp_plan_create: null index array");
 
   const dpp_config c = *cfg;
@@ -151,8 +152,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   if (c.head_dim != 128 && c.head_dim != 256)
     return fail(DPP_ERR_UNSUPPORTED, "head_dim " + std::to_string(c.head_dim) +
                                          " not built (128 and 256 are)");
-  if (c.page_size < 1 || c.page_size > 1024)
-    return fail(DPP_ERR_UNSUPPORTED, "page_size must be in [1, 1024]");
+  if (c.page_size < 0 || c.page_size > 1024)
+    return fail(DPP_ERR_UNSUPPORTED, "page_size must be in [1, 1024], or 0 for ragged KV");
   if (c.kv_dtype != DPP_KV_BF16 && c.kv_dtype != DPP_KV_FP8_E4M3)
     return fail(DPP_ERR_UNSUPPORTED, "kv_dtype must be DPP_KV_BF16 or DPP_KV_FP8_E4M3");
   if (!(c.sm_scale >= 0.f) || !std::isfinite(c.sm_scale))
@@ -164,7 +165,9 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   if (qo_indptr[0] != 0 || kv_indptr[0] != 0)
     return fail(DPP_ERR_INVALID, "qo_indptr[0] and kv_indptr[0] must be 0");
   const int32_t group = c.num_qo_heads / c.num_kv_heads;
-  const int64_t P = c.page_size;
+  const int64_t P = ragged ? kRaggedPage : c.page_size;
+  // ragged: a request's keys are addressed by 32-bit byte offsets from its first token
+  const int64_t token_bytes = (int64_t)c.num_kv_heads * c.head_dim * (c.kv_dtype == DPP_KV_FP8_E4M3 ? 1 : 2);
 
   const int32_t block_n = block_n_for(c.head_dim);
   const int32_t block_m = block_m_for(c.head_dim);
@@ -177,7 +180,12 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     if (qo_len < 0 || np < 0)
       return fail(DPP_ERR_INVALID, "indptr not non-decreasing at request " + std::to_string(r));
     int64_t kv_len = 0;
-    if (np > 0) {
+    if (ragged) {
+      kv_len = np;  // kv_indptr counts tokens
+      // (a load descriptor of the last KV tile may start up to one tile past kv_len)
+      if ((kv_len + 256) * token_bytes > std::numeric_limits<int32_t>::max())
+        return fail(DPP_ERR_UNSUPPORTED, "ragged request " + std::to_string(r) + " holds more than 2 GiB of K");
+    } else if (np > 0) {
       if (last_page_len[r] < 1 || last_page_len[r] > c.page_size)
         return fail(DPP_ERR_SHAPE, "kv_last_page_len[" + std::to_string(r) + "] = " +
                                        std::to_string(last_page_len[r]) + " outside [1, page_size]");
@@ -379,6 +387,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   plan->partial_lse_offset = header_bytes + align_up((size_t)max_used * c.head_dim * 4, 256);
   plan->workspace_bytes = plan->partial_lse_offset + align_up((size_t)max_used * 4, 256);
   plan->page_slots = (int32_t)max_page_span;
+  plan->ragged = ragged;
+  plan->total_kv_tokens = ragged && batch_size > 0 ? kv_indptr[batch_size] : 0;
   *out_plan = plan.release();
   return DPP_OK;
 }

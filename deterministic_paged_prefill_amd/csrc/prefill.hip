@@ -367,8 +367,10 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     kt0 = it.kv_tile_begin;
     n_tiles = it.kv_tile_end - kt0;  // >= 1
     page_span(u, key_lo_page, n_pages);
-    kbase = reinterpret_cast<const unsigned char*>(a.k_pool) + (int64_t)kvh * D * kElem;
-    vbase = reinterpret_cast<const unsigned char*>(a.v_pool) + (int64_t)kvh * D * kElem;
+    // ragged KV: the request's keys start at its first token (page_start), on page id 0
+    const int64_t base_off = (int64_t)kvh * D * kElem + (a.ragged ? (int64_t)rq.page_start * token_bytes : 0);
+    kbase = reinterpret_cast<const unsigned char*>(a.k_pool) + base_off;
+    vbase = reinterpret_cast<const unsigned char*>(a.v_pool) + base_off;
   };
   UnitRecord first = decode(rv);
   set_unit(first);
@@ -378,7 +380,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   auto load_page_ids = [&](const UnitRecord& u, int32_t* table) {
     int lo, n;
     page_span(u, lo, n);
-    const uint64_t src = reinterpret_cast<uint64_t>(a.kv_indices + u.req.page_start + lo);
+    // (ragged: one entry, read from the zero chunk a.kv_indices then points at)
+    const uint64_t src = reinterpret_cast<uint64_t>(a.kv_indices + (a.ragged ? 0 : u.req.page_start) + lo);
     const i32x4 rsrc = buffer_rsrc(uniform64(src), (uint32_t)__builtin_amdgcn_readfirstlane(n * 4));
     const uint32_t t0 = (uint32_t)(uintptr_t)table;
     for (int c = wave; c * 64 < n; c += C::WAVES) dma4_buf((c * 64 + lane) * 4, rsrc, t0 + (uint32_t)c * 256u);

@@ -37,6 +37,13 @@
  * owns no pages); token j lives in page kv_indices[kv_indptr[r] + j / page_size], slot
  * j % page_size. Slots past a request's kv_len are never read.
  *
+ * Ragged (contiguous) KV, page_size == 0 in the config (the non-paged prefill the sglang PR
+ * #46351 page names beside the paged one, "Motivation"): k_pool and v_pool are
+ * [total_tokens, num_kv_heads, head_dim]; kv_indptr counts tokens, request r's keys are rows
+ * kv_indptr[r] .. kv_indptr[r+1]-1; kv_last_page_len and kv_indices are ignored (may be
+ * NULL); num_pages in dpp_run is total_tokens. Same kernels, same arithmetic: a row's bits are
+ * those of the same row over a paged layout.
+ *
  * Errors: every entry point returns a dpp_status and, on failure, records a message that
  * dpp_last_error() returns (thread-local). Nothing aborts, exits or throws across the ABI.
  */
@@ -69,7 +76,7 @@ typedef struct {
   int32_t num_qo_heads;  /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;  /* Hkv */
   int32_t head_dim;      /* 128 or 256 */
-  int32_t page_size;     /* tokens per page, 1..1024 */
+  int32_t page_size;     /* tokens per page, 1..1024; 0 = ragged (contiguous) KV */
   int32_t kv_dtype;      /* dpp_kv_dtype */
   float sm_scale;        /* softmax scale; 0 selects 1/sqrt(head_dim) */
   float k_scale;         /* fp8 dequantisation multipliers (value = decode(code) * scale);
@@ -101,8 +108,10 @@ typedef struct {
  *   cfg                  model constants (copied)
  *   batch_size           B >= 0
  *   qo_indptr_host       [B+1] int32, qo_indptr[0] == 0, non-decreasing
- *   kv_indptr_host       [B+1] int32, kv_indptr[0] == 0, non-decreasing (page counts)
- *   kv_last_page_len_host[B]  int32, in [1, page_size] for every request with pages
+ *   kv_indptr_host       [B+1] int32, kv_indptr[0] == 0, non-decreasing (page counts; token
+ *                        counts for ragged KV, where a request's K may not exceed 2 GiB)
+ *   kv_last_page_len_host[B]  int32, in [1, page_size] for every request with pages (ignored,
+ *                        and may be NULL, for ragged KV)
  *   workspace_cap_bytes  upper bound on dpp_plan_workspace_bytes(); 0 = no bound. Rows whose
  *                        partials do not fit are run in further passes; the cap changes the
  *                        number of launches, never a bit of the result.
@@ -150,7 +159,9 @@ void dpp_plan_destroy(dpp_plan* plan);
  *
  *   q, k_pool, v_pool, kv_indices, o, lse   device pointers, layouts above
  *   q_rows        rows of q and o; must equal qo_indptr[B] of the plan (DPP_ERR_SHAPE)
- *   num_pages     pages in each pool; a page id outside [0, num_pages) reads as zeros
+ *   num_pages     pages in each pool; a page id outside [0, num_pages) reads as zeros. Ragged
+ *                 KV: the token rows of k_pool / v_pool; kv_indptr[B] above it is
+ *                 DPP_ERR_SHAPE, and kv_indices may be NULL
  *   workspace     device buffer of at least dpp_plan_workspace_bytes(plan) bytes, 256-byte
  *                 aligned; its contents are scratch (work list + split partials)
  *   flags         0, or DPP_RUN_REUSE_UPLOAD when dpp_plan_upload (or an earlier dpp_run) has

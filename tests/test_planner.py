@@ -299,7 +299,8 @@ def test_malformed_batches_are_rejected(dpp, mutate, status):
 @pytest.mark.parametrize("args,status", [
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=64), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=30, num_kv_heads=8, head_dim=128), "DPP_ERR_UNSUPPORTED"),
-    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=0), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=-1), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1025), "DPP_ERR_UNSUPPORTED"),
 ])
 def test_unsupported_configs(dpp, args, status):
     b = _specs_batch([(67, 3)])
@@ -356,3 +357,52 @@ def test_workload_batches_plan(dpp):
     work = wl.single_extend()
     p = _plan(dpp, work.batches["cached"])
     assert p.info.total_q_rows == 3
+
+
+# ---- ragged (contiguous) KV: page_size 0, kv_indptr in tokens
+
+def _ragged_indptr(specs):
+    kv_len = [kv for kv, _ in specs]
+    return np.concatenate([[0], np.cumsum(kv_len)]).astype(np.int32), kv_len
+
+
+@pytest.mark.parametrize("specs", [[(67, 3), (40, 40), (300, 0), (1, 1)], [(4100, 12), (8200, 2), (129, 129)]])
+def test_ragged_plan_has_the_paged_plans_work(dpp, specs):
+    """The same tiles, splits and items as the paged plan; each request's page_start is its
+    first token and its kv_len is its token count."""
+    b = _specs_batch(specs)
+    paged = parse(_plan(dpp, b).header())
+    kvp, kv_len = _ragged_indptr(specs)
+    rp = dpp.plan(32, 8, 128, 0, b.qo_indptr, kvp)  # no kv_last_page_len
+    ragged = parse(rp.header())
+    assert rp.info.workspace_bytes == _plan(dpp, b).info.workspace_bytes
+    assert list(ragged.requests[:, 3]) == kv_len
+    assert list(ragged.requests[:, 2]) == list(kvp[:-1])
+    assert (ragged.requests[:, [0, 1, 3]] == paged.requests[:, [0, 1, 3]]).all()
+    cols = [0, 1, 2, 3, 4, 5, 6, 8, 9, 11]  # everything but the page list offset
+    assert (ragged.items[:, cols] == paged.items[:, cols]).all()
+    assert (ragged.merges == paged.merges).all()
+
+
+def test_ragged_plan_ignores_last_page_len_and_checks_request_bytes(dpp):
+    qo = np.array([0, 2], dtype=np.int32)
+    a = dpp.plan(32, 8, 128, 0, qo, np.array([0, 100], dtype=np.int32), np.array([7], dtype=np.int32))
+    b = dpp.plan(32, 8, 128, 0, qo, np.array([0, 100], dtype=np.int32))
+    assert (a.header()[16:] == b.header()[16:]).all()
+    # 8 kv heads x 128 x 2 B = 2 KiB a token: a request's K plus one tile's worth of keys
+    # past its end must stay below 2 GiB
+    dpp.plan(32, 8, 128, 0, qo, np.array([0, (1 << 20) - 257], dtype=np.int32), workspace_cap=0)
+    with pytest.raises(dpp.DppValueError, match="DPP_ERR_UNSUPPORTED"):
+        dpp.plan(32, 8, 128, 0, qo, np.array([0, 1 << 20], dtype=np.int32), workspace_cap=0)
+    with pytest.raises(ValueError):
+        dpp.plan(32, 8, 128, 16, qo, np.array([0, 7], dtype=np.int32))  # paged needs last_page_len
+
+
+def test_ragged_run_rejects_kv_beyond_the_tokens_passed(dpp):
+    """Ragged KV: kv_indptr[-1] above the token rows the caller passes fails on the host."""
+    lib = dpp.library()
+    p = dpp.plan(32, 8, 128, 0, np.array([0, 3, 5], np.int32), np.array([0, 67, 107], np.int32))
+    fake = 1 << 20
+    ws = p.workspace_bytes
+    st = lib.dpp_run(p._h, fake, 5, fake, fake, 106, None, fake, fake, fake, ws, 0, None)
+    assert st == dpp.DPP_ERR_SHAPE and b"107 tokens" in lib.dpp_last_error()
