@@ -130,7 +130,11 @@ struct MergeItem {
   int32_t slot_base;
 };
 
-// Partial slot of (kv head c, split s, tile-local row lr) inside a tile's slot block.
+// Rows of a q tile's slot block per (kv head, split): the tile's rows rounded up to 16, so a
+// short tile (an extend or a one-token decode) does not hold a full tile's worth of slots.
+DPP_HOST_DEVICE constexpr int slot_rows_for(int tile_rows) { return (tile_rows + 15) / 16 * 16; }
+// Partial slot of (kv head c, split s, tile-local row lr) inside a tile's slot block, with
+// block_m = slot_rows_for(the tile's rows).
 DPP_HOST_DEVICE inline int64_t partial_slot(int32_t slot_base, int32_t tile_splits, int c, int s,
                                             int lr, int block_m) {
   return (int64_t)slot_base + ((int64_t)c * tile_splits + s) * block_m + lr;

@@ -95,6 +95,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int tile_rows = min(a.block_m, rq.qo_len * g - mi.row_start);
   const int ctx = rq.kv_len - rq.qo_len;
   const int col = (threadIdx.x % kTpr) * 4;
+  const int stride = slot_rows_for(tile_rows);
   for (int lr = threadIdx.x / kTpr; lr < tile_rows; lr += kRowsPerPass) {
     const int R = mi.row_start + lr;
     const int token = R / g;
@@ -102,10 +103,10 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
     const int S = p / kSplitTokens + 1;
     if (S < 2) continue;  // finished by the prefill kernel
     auto lse_at = [&](int s) {
-      return a.part_lse2[partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr, a.block_m)];
+      return a.part_lse2[partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr, stride)];
     };
     auto o_at = [&](int s) {
-      return *reinterpret_cast<const f32x4*>(a.part_o + partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr, a.block_m) * D + col);
+      return *reinterpret_cast<const f32x4*>(a.part_o + partial_slot(mi.slot_base, mi.tile_splits, kvh, s, lr, stride) * D + col);
     };
     float lse2;
     const f32x4 o = merge4(S, lse_at, o_at, &lse2);

@@ -237,11 +237,12 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
     slot_limit = std::min<int64_t>(slot_limit, max_slots_for(workspace_cap - header_bytes_max, c.head_dim));
   }
 
-  // Passes: tiles in request order; a tile needing partials takes S_t * Hkv * block_m slots.
+  // Passes: tiles in request order; a tile needing partials takes S_t * Hkv * slot_rows_for(rows)
+  // slots.
   int32_t pass = 0;
   int64_t used = 0, max_used = 0;
   for (auto& t : tiles) {
-    const int64_t need = t.splits > 1 ? (int64_t)t.splits * c.num_kv_heads * block_m : 0;
+    const int64_t need = t.splits > 1 ? (int64_t)t.splits * c.num_kv_heads * slot_rows_for(t.rows) : 0;
     if (need > slot_limit)
       return fail(DPP_ERR_WORKSPACE,
                   "workspace cap too small: one q tile needs " +

@@ -700,7 +700,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         }
       } else if (mine) {
         // a row reaching past the first split: its fp32 partial, straight from the MFMA layout
-        const int64_t slot = partial_slot(e.slot_base, e.tile_splits, e.kv_head, e.split, lr, C::PLAN_BM);
+        const int64_t slot = partial_slot(e.slot_base, e.tile_splits, e.kv_head, e.split, lr, slot_rows_for(e_rows));
         DPP_GLOBAL float* pp = part_o_out + slot * D + vh * (D / 2) + 4 * lg;
 #pragma unroll
         for (int db = 0; db < VDB; ++db)

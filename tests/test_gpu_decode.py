@@ -5,7 +5,8 @@ in ascending split order.
 Checks: every row against the fp64 oracle (max |o - oracle| <= 1e-2, max |lse - oracle| <=
 2e-3); each decode row bit-identical to the last row of its prompt's full prefill; the batch's
 bits unchanged by running each request alone, by reversing the batch and by a workspace cap
-that cuts the batch into several passes.
+that cuts the batch into several passes. A one-token row's partials take 16 slot rows per
+(kv head, split), not a full tile's 256: the whole batch plans into 5.6 MB.
 """
 import numpy as np
 import pytest
@@ -72,11 +73,12 @@ def test_decode_alone_and_reversed(work, dev, decoded):
 
 def test_decode_workspace_cap_passes(work, dev, decoded):
     dec = work.batches["decode"]
-    plan = dev.plan(dec, cap=40 << 20)
-    say(f"decode batch under a 40 MiB cap: {plan.info.num_passes} passes, "
+    assert dev.plan(dec).info.workspace_bytes < 6 << 20
+    plan = dev.plan(dec, cap=3 << 20)
+    say(f"decode batch under a 3 MiB cap: {plan.info.num_passes} passes, "
         f"workspace {plan.info.workspace_bytes} B")
     assert plan.info.num_passes > 1
-    assert plan.info.workspace_bytes <= 40 << 20
+    assert plan.info.workspace_bytes <= 3 << 20
     o, l = dev.run(dec, plan=plan)
     assert_bits_equal(o, decoded[0], "capped o")
     assert_bits_equal(l, decoded[1], "capped lse")

@@ -142,7 +142,7 @@ def test_workspace_closed_form_single_pass(dpp):
             S = pmax // 4096 + 1
             ntile += 1
             if S > 1:
-                slots += S * 8 * bm
+                slots += S * 8 * (-(-rows // 16) * 16)  # the tile's rows, rounded up to 16
     # every tile is wide: each (item, kv head) also has a unit record of the persistent launch
     assert len(parsed.units) == 8 * len(parsed.items)
     words = 16 + 4 * len(specs) + 16 * len(parsed.items) + 4 * len(parsed.merges) + 16 * len(parsed.units)
