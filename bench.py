@@ -68,7 +68,7 @@ def kv_bytes(batch, hkv: int, d: int, elem: int) -> int:
 class Runner:
     """Pre-resolved dpp_run arguments so the timed loop is one C call per step."""
 
-    def __init__(self, work, batch, replicas: int = 1, cap: int = 256 << 20):
+    def __init__(self, work, batch, replicas: int = 1, cap: int = 256 << 20, adaptive: bool = False):
         import torch
 
         import deterministic_paged_prefill_amd as dpp
@@ -80,7 +80,7 @@ class Runner:
         self.plan = dpp.plan(work.num_qo_heads, work.num_kv_heads, work.head_dim, work.page_size,
                              batch.qo_indptr, batch.kv_indptr, batch.kv_last_page_len,
                              kv_dtype=work.kv_dtype, k_scale=work.k_scale, v_scale=work.v_scale,
-                             workspace_cap=cap)
+                             workspace_cap=cap, adaptive_kv_tile=adaptive)
         self.plan_us = (time.perf_counter() - t0) * 1e6
         dev = torch.device("cuda")
         P = work.num_pages
@@ -248,6 +248,20 @@ def main() -> int:
         result["extend"]["radix_logical_gbps"] = kv_bytes(work_r.batches["cached"], hkv, d, 2) / (ms_r * 1e-3) / 1e9
         result["extend"]["radix_ms"] = ms_r
         del rr, run
+        # negative control: the same extend batch planned with a batch-dependent KV tile
+        ra = Runner(work, cached, replicas=args.replicas, adaptive=True)
+        o_a, l_a = ra.outputs(0)
+        fa = Runner(work, full, replicas=1, adaptive=True)
+        o_fa, l_fa = fa.outputs(0)
+        da_o = da_l = 0.0
+        for r in range(cached.batch_size):
+            ia, ib = wl.matching_rows(cached, r, full, r)
+            da_o = max(da_o, float((o_a[ia].float() - o_fa[ib].float()).abs().max()))
+            da_l = max(da_l, float((l_a[ia] - l_fa[ib]).abs().max()))
+        ms_a, _ = ra.timed(args.steps, args.warmup)
+        result["extend"]["adaptive"] = dict(ms=ms_a, block_n=ra.plan.info.block_n,
+                                            full_block_n=fa.plan.info.block_n, max_o=da_o, max_l=da_l)
+        del ra, fa
 
     # ---------------------------------------------------------------- cold prefill
     if args.only in (None, "prefill") and not args.no_prefill:
@@ -315,6 +329,14 @@ def main() -> int:
                           "upload_us": round(ext["upload_us"], 1),
                           "radix_layout_logical_gbps": round(ext["radix_logical_gbps"], 1),
                           "radix_layout_us_per_step": round(ext["radix_ms"] * 1e3, 2)},
+        "adaptive_tile_control": {
+            "what": "the same extend batch planned with a KV tile picked from the batch (FlashInfer's "
+                    "average-packed-length rule; NOT batch invariant), against its full prefills",
+            "block_n": ext["adaptive"]["block_n"], "full_prefill_block_n": ext["adaptive"]["full_block_n"],
+            "us_per_step": round(ext["adaptive"]["ms"] * 1e3, 2),
+            "cached_vs_full_max_abs_diff_o": ext["adaptive"]["max_o"],
+            "cached_vs_full_max_abs_diff_lse": ext["adaptive"]["max_l"],
+            "invariance_cost": round(ext["ms"] / ext["adaptive"]["ms"] - 1.0, 4)},
         "kernel_source_sha256_16": kernel_hash(),
     }
     if "prefill" in result:

@@ -38,6 +38,7 @@ def tile_shape(head_dim: int) -> tuple:
 
 DPP_OK, DPP_ERR_INVALID, DPP_ERR_SHAPE, DPP_ERR_UNSUPPORTED, DPP_ERR_WORKSPACE, DPP_ERR_HIP = range(6)
 RUN_REUSE_UPLOAD = 1
+PLAN_ADAPTIVE_KV_TILE = 1  # comparison mode: NOT batch invariant (see include/dpp.h)
 KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -85,7 +86,7 @@ class PlanInfo:
 
 
 _lib = None
-EXPORTS = ("dpp_plan_create", "dpp_plan_workspace_bytes", "dpp_plan_get_info", "dpp_plan_header",
+EXPORTS = ("dpp_plan_create", "dpp_plan_create_ex", "dpp_plan_workspace_bytes", "dpp_plan_get_info", "dpp_plan_header",
            "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_merge_states", "dpp_last_error",
            "dpp_status_string", "dpp_abi_version")
 
@@ -102,6 +103,9 @@ def library():
     vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.dpp_plan_create.restype = ctypes.c_int
     lib.dpp_plan_create.argtypes = [ctypes.POINTER(_Config), i32, vp, vp, vp, sz, ctypes.POINTER(vp)]
+    lib.dpp_plan_create_ex.restype = ctypes.c_int
+    lib.dpp_plan_create_ex.argtypes = [ctypes.POINTER(_Config), i32, vp, vp, vp, sz, ctypes.c_uint32,
+                                       ctypes.POINTER(vp)]
     lib.dpp_plan_workspace_bytes.restype = sz
     lib.dpp_plan_workspace_bytes.argtypes = [vp]
     lib.dpp_plan_get_info.restype = ctypes.c_int
@@ -262,8 +266,11 @@ class Plan:
 def plan(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, qo_indptr,
          kv_indptr, kv_last_page_len=None, *, kv_dtype: str = "bf16", sm_scale: float | None = None,
          k_scale: float = 1.0, v_scale: float = 1.0,
-         workspace_cap: int = DEFAULT_WORKSPACE_CAP) -> Plan:
-    """Plan one batch from host copies of its index arrays (no GPU work)."""
+         workspace_cap: int = DEFAULT_WORKSPACE_CAP, adaptive_kv_tile: bool = False) -> Plan:
+    """Plan one batch from host copies of its index arrays (no GPU work).
+
+    ``adaptive_kv_tile=True`` is the comparison mode that picks the KV tile from the batch
+    (dpp_plan_create_ex with DPP_PLAN_ADAPTIVE_KV_TILE): NOT batch invariant."""
     if kv_dtype not in KV_DTYPES:
         raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
     qo, kvp = _i32(qo_indptr), _i32(kv_indptr)
@@ -279,8 +286,10 @@ def plan(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, qo
                   0.0 if sm_scale is None else float(sm_scale), float(k_scale), float(v_scale))
     h = ctypes.c_void_p()
     last_ptr = last.ctypes.data if batch > 0 else None
-    _check(library().dpp_plan_create(ctypes.byref(cfg), batch, qo.ctypes.data, kvp.ctypes.data,
-                                     last_ptr, int(workspace_cap), ctypes.byref(h)))
+    _check(library().dpp_plan_create_ex(ctypes.byref(cfg), batch, qo.ctypes.data, kvp.ctypes.data,
+                                        last_ptr, int(workspace_cap),
+                                        PLAN_ADAPTIVE_KV_TILE if adaptive_kv_tile else 0,
+                                        ctypes.byref(h)))
     return Plan(h, cfg, batch)
 
 

@@ -146,7 +146,7 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
       a.chain_offset = narrow ? -1 : plan->chain_offset[(size_t)p];
       a.num_chains = narrow ? 0 : plan->chain_blocks[(size_t)p];
       if (a.num_items > 0) {
-        e = launch_prefill(a, plan->cfg.head_dim, plan->cfg.kv_dtype, narrow != 0, stream);
+        e = launch_prefill(a, plan->cfg.head_dim, plan->cfg.kv_dtype, narrow != 0, plan->block_n, stream);
         if (e != hipSuccess) return hip_fail(e, "prefill launch");
       }
     }

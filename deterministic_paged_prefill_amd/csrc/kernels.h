@@ -9,8 +9,10 @@ namespace dpp {
 
 // Prefill items of one pass: num_items * num_kv_heads blocks of 64 * waves_for(head_dim)
 // threads, dynamic LDS for the tile buffers and the item's page-id table. `narrow` selects the
-// instantiation for tiles of at most kNarrowRows rows.
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool narrow, hipStream_t stream);
+// instantiation for tiles of at most kNarrowRows rows; block_n is the plan's KV tile
+// (block_n_for(head_dim), or 32 for narrow bf16 tiles of an adaptive-tile comparison plan).
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool narrow, int block_n,
+                          hipStream_t stream);
 
 // Merge of the split partials of one pass: grid (num_merges, num_kv_heads).
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream);

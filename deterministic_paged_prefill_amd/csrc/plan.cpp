@@ -137,7 +137,16 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
                                       const int32_t* qo_indptr, const int32_t* kv_indptr,
                                       const int32_t* last_page_len, size_t workspace_cap,
                                       dpp_plan** out_plan) {
+  return dpp_plan_create_ex(cfg, batch_size, qo_indptr, kv_indptr, last_page_len, workspace_cap, 0u, out_plan);
+}
+
+extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_size,
+                                         const int32_t* qo_indptr, const int32_t* kv_indptr,
+                                         const int32_t* last_page_len, size_t workspace_cap,
+                                         uint32_t plan_flags, dpp_plan** out_plan) {
   if (out_plan) *out_plan = nullptr;
+  if (plan_flags & ~(uint32_t)DPP_PLAN_ADAPTIVE_KV_TILE)
+    return fail(DPP_ERR_INVALID, "dpp_plan_create_ex: unknown plan flags");
   if (!cfg || !out_plan) return fail(DPP_ERR_INVALID, "dpp_plan_create: null cfg or out_plan");
   if (batch_size < 0) return fail(DPP_ERR_INVALID, "dpp_plan_create: negative batch_size");
   const bool ragged = cfg && cfg->page_size == 0;
@@ -169,9 +178,8 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   // ragged: a request's keys are addressed by 32-bit byte offsets from its first token
   const int64_t token_bytes = (int64_t)c.num_kv_heads * c.head_dim * (c.kv_dtype == DPP_KV_FP8_E4M3 ? 1 : 2);
 
-  const int32_t block_n = block_n_for(c.head_dim);
+  int32_t block_n = block_n_for(c.head_dim);
   const int32_t block_m = block_m_for(c.head_dim);
-  const int32_t tiles_per_split = kSplitTokens / block_n;
   std::vector<RequestDesc> reqs((size_t)batch_size);
   std::vector<TileInfo> tiles;
   for (int32_t r = 0; r < batch_size; ++r) {
@@ -210,6 +218,21 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
       tiles.push_back(t);
     }
   }
+
+  // Adaptive-tile comparison mode (never batch invariant): FlashInfer's rule on the sglang PR
+  // #46351 page ("Root cause"; the author's A100 findings) gives a 16-row q tile when the
+  // batch's average packed query length sum(qo_len * group) / batch_size is at most 16, and
+  // the tile moves the reduction split. Here the q tile never touches a row's arithmetic, so
+  // the mode moves what does: such a batch of narrow tiles runs with 32-key KV tiles at
+  // head_dim 128 instead of 64, and its rows stop matching the same rows of a larger batch.
+  if ((plan_flags & DPP_PLAN_ADAPTIVE_KV_TILE) && c.head_dim == 128 && c.kv_dtype == DPP_KV_BF16 &&
+      batch_size > 0 && !tiles.empty()) {
+    int64_t packed = 0;
+    for (int32_t r = 0; r < batch_size; ++r) packed += (int64_t)reqs[(size_t)r].qo_len * group;
+    const bool all_narrow = std::all_of(tiles.begin(), tiles.end(), [](const TileInfo& t) { return t.rows <= kNarrowRows; });
+    if (all_narrow && packed <= 16 * (int64_t)batch_size) block_n = 32;
+  }
+  const int32_t tiles_per_split = kSplitTokens / block_n;
 
   int64_t n_items = 0, n_merges = 0;
   for (const auto& t : tiles) {
@@ -389,6 +412,7 @@ extern "C" dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
   plan->workspace_bytes = plan->partial_lse_offset + align_up((size_t)max_used * 4, 256);
   plan->page_slots = (int32_t)max_page_span;
   plan->ragged = ragged;
+  plan->block_n = block_n;
   plan->total_kv_tokens = ragged && batch_size > 0 ? kv_indptr[batch_size] : 0;
   *out_plan = plan.release();
   return DPP_OK;
@@ -401,7 +425,7 @@ extern "C" size_t dpp_plan_workspace_bytes(const dpp_plan* plan) {
 extern "C" dpp_status dpp_plan_get_info(const dpp_plan* plan, dpp_plan_info* info) {
   if (!plan || !info) return fail(DPP_ERR_INVALID, "dpp_plan_get_info: null argument");
   info->block_m = block_m_for(plan->cfg.head_dim);
-  info->block_n = block_n_for(plan->cfg.head_dim);
+  info->block_n = plan->block_n;
   info->split_tokens = kSplitTokens;
   info->num_passes = (int32_t)plan->item_pass.size() - 1;
   info->num_prefill_items = plan->num_items;
@@ -434,4 +458,4 @@ extern "C" const char* dpp_status_string(dpp_status st) {
   return "DPP_ERR_UNKNOWN";
 }
 
-extern "C" int32_t dpp_abi_version(void) { return 1; }
+extern "C" int32_t dpp_abi_version(void) { return 2; }

@@ -41,6 +41,8 @@ struct dpp_plan {
   size_t workspace_bytes = 0;
   int32_t page_slots = 0;         // LDS page-id entries one item may need
   bool ragged = false;            // page_size 0: contiguous KV, kv_indptr counts tokens
+  int32_t block_n = 0;            // keys per KV tile: block_n_for(head_dim), except in the
+                                  // adaptive-tile comparison mode
   int64_t total_kv_tokens = 0;    // ragged: kv_indptr[B], the KV rows the kernels may read
   int32_t item_offset = 0;        // word offset of the item records in the header
   uint32_t plan_id = 0;           // stamped into the work list

@@ -66,13 +66,15 @@ constexpr float kRebase = 8.0f;
 template <int NB>
 constexpr int ahead_for() { return NB == 1 ? 7 : 3; }
 
-template <int D, int NB>
+// BNX: keys per KV tile. block_n_for(D) in every batch-invariant plan; a plan in the
+// adaptive-tile comparison mode runs narrow tiles with 32 keys at D = 128.
+template <int D, int NB, int BNX = block_n_for(D)>
 struct Geo {
   static constexpr int WAVES = waves_for(D);
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int PLAN_BM = block_m_for(D);   // packed rows of a planned q tile
   static constexpr int RPW = 16 * NB;              // rows this instantiation gives a wave
-  static constexpr int BN = block_n_for(D);        // keys per KV tile
+  static constexpr int BN = BNX;                   // keys per KV tile
   static constexpr int CH = D / 8;                 // 16-byte bf16 chunks per K/V row
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one KV tile of K or V in bf16
@@ -84,7 +86,7 @@ struct Geo {
   static constexpr int NCH = BN * CH / THREADS;    // 16-byte chunks per thread per tensor per tile
   static constexpr int KPI = 64 * 16 / ROW_BYTES;  // key rows one wave-wide DMA load covers
   static constexpr int LDS_BYTES = 2 * NBUF * TILE_BYTES;
-  static_assert(LDS_BYTES == ring_bytes_for(D), "ring size");
+  static_assert(BN != block_n_for(D) || LDS_BYTES == ring_bytes_for(D), "ring size");
   // narrow bf16 kernel: P^T and alpha of two tiles, then l and m, passed between two waves
   static constexpr int XSLOT = 64 * KC * 16 + 64 * 4;
   static constexpr int XBYTES = 2 * XSLOT + 2 * 64 * 4;
@@ -236,9 +238,9 @@ constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2;
 // all of K; each loads only its half of V's columns and writes its half of the output. Every
 // output element still accumulates the same MFMA sequence, so the bits are those of one
 // workgroup; the unit's bytes per workgroup drop to 3/4 and twice the workgroups stream them.
-template <int D, bool FP8, int NB, int MODE, bool VH>
+template <int D, bool FP8, int NB, int MODE, bool VH, int BNX>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
-  using C = Geo<D, NB>;
+  using C = Geo<D, NB, BNX>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // Narrow bf16 kernel with eight waves: wave 0 computes scores and softmax, wave 4 (on the
   // same SIMD) the output, and waves 2, 3, 6, 7 issue the DMA loads.
@@ -1127,9 +1129,9 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   }
 }
 
-template <int D, bool FP8, int NB, int MODE, bool VH = false>
+template <int D, bool FP8, int NB, int MODE, bool VH = false, int BNX = block_n_for(D)>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
-  using C = Geo<D, NB>;
+  using C = Geo<D, NB, BNX>;
   constexpr int kRing = C::NBUF * (C::TILE_BYTES + (VH ? C::TILE_BYTES / 2 : C::TILE_BYTES));
   // page-id tables (4 bytes an entry): a unit's pages plus one tile's worth of slack for the
   // last tile's lookups past kv_len (their chunks read the zero chunk); two in a persistent
@@ -1142,7 +1144,7 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   if (lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE, VH>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE, VH, BNX>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
@@ -1150,7 +1152,7 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   if (VH && a.chain_offset >= 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains : (VH ? 2 : 1) * a.num_items * a.num_kv_heads));
   if (a.chain_offset >= 0 && !chained_launch(D, FP8, NB == 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE, VH>), grid, dim3(C::THREADS), lds, stream, a);
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE, VH, BNX>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1168,13 +1170,17 @@ int compute_units() {
   return v;
 }
 
-template <int D, int NB>
+template <int D, int NB, int BNX = block_n_for(D)>
 hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   const int P = a.page_size;
   const bool pow2 = (P & (P - 1)) == 0;
-  if (fp8) {
-    return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, kPagesPow2>(a, stream)
-                                       : launch_one<D, true, NB, kPagesGeneral>(a, stream);
+  if constexpr (BNX == block_n_for(D)) {
+    if (fp8) {
+      return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, kPagesPow2>(a, stream)
+                                         : launch_one<D, true, NB, kPagesGeneral>(a, stream);
+    }
+  } else if (fp8) {
+    return hipErrorInvalidValue;  // the comparison tile is built for bf16 only
   }
   // The narrow kernel's issuing waves compute nothing else: per-lane (vector) addresses
   // suit them. The wide kernel's waves are busy with the softmax: scalar descriptors.
@@ -1185,12 +1191,12 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
     // two workgroups per unit (same bits; a unit streams K/V at the rate one CU sustains, so
     // the otherwise idle CUs take a quarter of its bytes each).
     if (2 * a.num_items * a.num_kv_heads <= compute_units()) {
-      return pow2 && P <= block_n_for(D) ? launch_one<D, false, NB, kPagesPow2, true>(a, stream)
-                                         : launch_one<D, false, NB, kPagesGeneral, true>(a, stream);
+      return pow2 && P <= BNX ? launch_one<D, false, NB, kPagesPow2, true, BNX>(a, stream)
+                              : launch_one<D, false, NB, kPagesGeneral, true, BNX>(a, stream);
     }
   }
-  return pow2 && P <= block_n_for(D) ? launch_one<D, false, NB, kPagesPow2>(a, stream)
-                                     : launch_one<D, false, NB, kPagesGeneral>(a, stream);
+  return pow2 && P <= BNX ? launch_one<D, false, NB, kPagesPow2, false, BNX>(a, stream)
+                          : launch_one<D, false, NB, kPagesGeneral, false, BNX>(a, stream);
 }
 
 template <int D>
@@ -1201,8 +1207,14 @@ hipError_t launch_d(const PrefillArgs& a, bool fp8, bool narrow, hipStream_t str
 
 }  // namespace
 
-hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool narrow, hipStream_t stream) {
+hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool narrow, int block_n,
+                          hipStream_t stream) {
   const bool fp8 = kv_dtype == 1;
+  if (block_n != block_n_for(head_dim)) {
+    // adaptive-tile comparison plans only: narrow bf16 tiles with 32 keys at head_dim 128
+    if (head_dim == 128 && block_n == 32 && narrow && !fp8) return launch_nb<128, 1, 32>(a, false, stream);
+    return hipErrorInvalidValue;
+  }
   if (head_dim == 128) return launch_d<128>(a, fp8, narrow, stream);
   if (head_dim == 256) return launch_d<256>(a, fp8, narrow, stream);
   return hipErrorInvalidValue;

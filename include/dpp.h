@@ -126,6 +126,25 @@ dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
                            const int32_t* kv_last_page_len_host, size_t workspace_cap_bytes,
                            dpp_plan** out_plan);
 
+/* dpp_plan_create_ex flags */
+#define DPP_PLAN_ADAPTIVE_KV_TILE 1u
+
+/*
+ * dpp_plan_create with plan flags (0: identical to dpp_plan_create). DPP_PLAN_ADAPTIVE_KV_TILE
+ * is a comparison mode that gives up batch invariance on purpose: like FlashInfer's tile rule
+ * (the sglang PR #46351 page, "Root cause" and the author's A100 findings: a 16-row q tile when
+ * the batch's average packed query length sum(qo_len * group) / batch_size is at most 16), a
+ * batch whose tiles all have at most 16 packed rows and whose average is at most 16 runs with
+ * 32-key KV tiles at head_dim 128 (bf16) instead of 64. Such a batch's rows then differ in
+ * their last bits from the same rows planned in a larger batch; it exists to measure that
+ * difference and what the fixed tile costs. dpp_plan_info.block_n reports the tile used.
+ * Errors: those of dpp_plan_create, and DPP_ERR_INVALID for unknown flag bits.
+ */
+dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_size,
+                              const int32_t* qo_indptr_host, const int32_t* kv_indptr_host,
+                              const int32_t* kv_last_page_len_host, size_t workspace_cap_bytes,
+                              uint32_t plan_flags, dpp_plan** out_plan);
+
 /* Bytes of device workspace dpp_run needs for this plan (256-byte aligned buffer). */
 size_t dpp_plan_workspace_bytes(const dpp_plan* plan);
 

@@ -34,7 +34,7 @@ class Device:
 
     def run(self, batch, cap=None, plan=None, q=None):
         say(f"run {self.work.name}: B={batch.batch_size} rows={batch.num_q_tokens} "
-            f"cap={cap}")
+            f"cap={cap} block_n={plan.info.block_n if plan else 'default'}")
         p = plan or self.plan(batch, cap)
         qd = (batch.q if q is None else q).cuda()
         kvi = torch.from_numpy(batch.kv_indices).cuda()

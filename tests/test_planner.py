@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(dpp):
     assert declared, "no declarations parsed"
     assert declared <= exported, declared - exported
     assert declared == set(dpp.EXPORTS)
-    assert dpp.library().dpp_abi_version() == 1
+    assert dpp.library().dpp_abi_version() == 2
 
 
 def _plan(dpp, batch, hq=32, hkv=8, d=128, page=16, cap=0, **kw):
@@ -406,3 +406,36 @@ def test_ragged_run_rejects_kv_beyond_the_tokens_passed(dpp):
     ws = p.workspace_bytes
     st = lib.dpp_run(p._h, fake, 5, fake, fake, 106, None, fake, fake, fake, ws, 0, None)
     assert st == dpp.DPP_ERR_SHAPE and b"107 tokens" in lib.dpp_last_error()
+
+
+# ---- adaptive-tile comparison mode (not batch invariant)
+
+def test_adaptive_tile_mode_picks_the_kv_tile_from_the_batch(dpp):
+    """FlashInfer's rule: an average packed query length of at most 16 over a batch of narrow
+    tiles gets 32-key KV tiles at head_dim 128; anything else, and the default mode, 64."""
+    extend = _specs_batch([(1025, 1), (1026, 2), (1028, 4), (1027, 3)])  # avg packed 10
+    longer = _specs_batch([(1025, 4), (1026, 4), (1028, 4), (1027, 5)])  # avg packed 17
+    prefill = _specs_batch([(1028, 1028)])
+    ad = lambda b: _plan(dpp, b, adaptive_kv_tile=True)
+    assert _plan(dpp, extend).info.block_n == 64
+    p = ad(extend)
+    assert p.info.block_n == 32
+    items = parse(p.header()).items
+    fixed = parse(_plan(dpp, extend).header()).items
+    # the same items, their KV tiles counted in 32-key units: 1028 keys -> 33 tiles, not 17
+    assert (items[:, 5] == [-(-(kv) // 32) for kv in (1025, 1026, 1028, 1027)]).all()
+    assert (fixed[:, 5] == [-(-(kv) // 64) for kv in (1025, 1026, 1028, 1027)]).all()
+    assert ad(longer).info.block_n == 64 and ad(prefill).info.block_n == 64
+    # head_dim 256 keeps its 32-key tile, fp8 its own
+    assert _plan(dpp, extend, hq=24, hkv=4, d=256, adaptive_kv_tile=True).info.block_n == 32
+    assert _plan(dpp, extend, kv_dtype="fp8_e4m3", adaptive_kv_tile=True).info.block_n == 64
+
+
+def test_plan_create_ex_rejects_unknown_flags(dpp):
+    lib = dpp.library()
+    b = _specs_batch([(67, 3)])
+    cfg = dpp._Config(32, 8, 128, 16, 0, 0.0, 1.0, 1.0)
+    h = ctypes.c_void_p()
+    st = lib.dpp_plan_create_ex(ctypes.byref(cfg), 1, b.qo_indptr.ctypes.data, b.kv_indptr.ctypes.data,
+                                b.kv_last_page_len.ctypes.data, 0, 2, ctypes.byref(h))
+    assert st == dpp.DPP_ERR_INVALID and h.value is None
