@@ -145,7 +145,9 @@ __global__ __launch_bounds__(kMergeThreads) void merge_dense_kernel(MergeDenseAr
 
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream) {
   dim3 grid((unsigned)a.num_merges, (unsigned)num_kv_heads);
-  if (head_dim == 128)
+  if (head_dim == 64)
+    hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, a);
+  else if (head_dim == 128)
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 256)
     hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kMergeThreads), 0, stream, a);

@@ -93,29 +93,33 @@ struct Geo {
   static_assert(NCH * THREADS == BN * CH, "the threads cover a tile");
   static_assert(NCH * 64 * WAVES * 16 == TILE_BYTES, "one DMA load per wave moves 1 KiB");
   static_assert(RPW * WAVES >= kNarrowRows && RPW * WAVES <= PLAN_BM, "tile rows fit the waves");
-  static_assert(CH >= 16, "swizzle needs 16 chunks per row");
+  static_assert(CH >= 8, "swizzles need 8 chunks per row");
   static_assert(KC >= 1 && KB == 2 * KC, "tile shape");
 };
 
-// Byte offset of 16-byte chunk c of key row `key` inside the K tile. The XOR with key % 16
-// spreads the 16 key rows one QK^T operand read touches (same chunk) over all banks.
+// K tile: 16-byte chunk c of key row `key` sits at chunk c ^ kswz(key). The XOR with key % 16
+// (key % 8 for 128-byte rows, head_dim 64) spreads the key rows one QK^T operand read touches
+// (same chunk) over the banks.
+template <int ROW_BYTES>
+__device__ constexpr int kswz(int key) {
+  return key & ((ROW_BYTES / 16 < 16 ? ROW_BYTES / 16 : 16) - 1);
+}
 template <int ROW_BYTES>
 __device__ inline int chunk_off(int key, int c) {
-  return key * ROW_BYTES + ((c ^ (key & 15)) << 4);
+  return key * ROW_BYTES + ((c ^ kswz<ROW_BYTES>(key)) << 4);
 }
-// Same for the V tile, swizzled in 32-byte units: a transposing read takes 32 bytes from each
-// of 4 consecutive keys per 16 lanes (8 keys per 32 lanes), which this spreads over all banks.
+// V tile, swizzled in 32-byte units: a transposing read takes 32 bytes from each of 4
+// consecutive keys per 16 lanes (8 keys per 32 lanes). Rows of 256 bytes or more move unit u
+// to u ^ (key % 8); rows of 128 bytes (head_dim 64, or half of head_dim 128 with VH) to
+// u ^ ((key / 2) % 4), so the 8 keys of a half-wave land on 8 distinct 32-byte bank groups.
+template <int ROW_BYTES>
+__device__ constexpr int vswz(int key) {
+  static_assert(ROW_BYTES >= 128, "V rows of at least 128 bytes");
+  return ROW_BYTES >= 256 ? (key & 7) << 1 : ((key >> 1) & 3) << 1;
+}
 template <int ROW_BYTES>
 __device__ inline int chunk_off_v(int key, int c) {
-  return key * ROW_BYTES + ((c ^ ((key & 7) << 1)) << 4);
-}
-
-// Same for a V tile of half-width rows (head_dim D/2, 128 bytes at D = 128): 32-byte unit u of
-// key row `key` sits at unit u ^ ((key / 2) % 4), so the 8 keys a half-wave's transposing read
-// touches (32 bytes each) land on 8 distinct 32-byte bank groups.
-template <int ROW_BYTES>
-__device__ inline int chunk_off_vh(int key, int c) {
-  return key * ROW_BYTES + ((c ^ (((key >> 1) & 3) << 1)) << 4);
+  return key * ROW_BYTES + ((c ^ vswz<ROW_BYTES>(key)) << 4);
 }
 
 // OCP E4M3 code -> fp32 (exact): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
@@ -456,8 +460,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       const int q = (i * IW + iw) * 64 + lane;
       krow[i] = q / C::CH;
       const int slot = q % C::CH;
-      c_k = slot ^ (krow[i] & 15);         // chunk_off(key, c_k) == 16 q
-      c_v = slot ^ ((krow[i] & 7) << 1);   // chunk_off_v(key, c_v) == 16 q
+      c_k = slot ^ kswz<C::ROW_BYTES>(krow[i]);  // chunk_off(key, c_k) == 16 q
+      c_v = slot ^ vswz<C::ROW_BYTES>(krow[i]);  // chunk_off_v(key, c_v) == 16 q
       lds_k[i] = lds_v[i] = 0;
     }
     kcol[i] = c_k * 8 * kElem;
@@ -478,7 +482,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       constexpr int HCH = C::CH / 2;
       vrow[i] = q / HCH;
       const int slot = q % HCH;
-      vcolh[i] = (vh * HCH + (slot ^ (((vrow[i] >> 1) & 3) << 1))) * 8 * kElem;  // chunk_off_vh(.) == 16 q
+      vcolh[i] = (vh * HCH + (slot ^ vswz<VROW>(vrow[i]))) * 8 * kElem;  // chunk_off_v<VROW>(.) == 16 q
     } else {
       vrow[i] = krow[i];
       vcolh[i] = vcol[i];
@@ -854,7 +858,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       for (int h = 0; h < 2; ++h) {
         const int key = kc * 32 + h * 16 + lg * 4 + (li >> 2);
         const int e = db * 16 + 4 * (li & 3);
-        const int off = VH ? chunk_off_vh<VROW>(key, e >> 3) : chunk_off_v<VROW>(key, e >> 3);
+        const int off = chunk_off_v<VROW>(key, e >> 3);
         const unsigned char* addr = v_lds + off + (e & 7) * 2;
         hv[h] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((DPP_LDS s16x4*)(addr));
       }
@@ -1186,7 +1190,7 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   // suit them. The wide kernel's waves are busy with the softmax: scalar descriptors.
   if constexpr (NB > 1) {
     if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
-  } else if constexpr (waves_for(D) == 8) {
+  } else if constexpr (waves_for(D) == 8 && D >= 128) {
     // A narrow launch of at most one unit per two compute units splits head_dim in PV over
     // two workgroups per unit (same bits; a unit streams K/V at the rate one CU sustains, so
     // the otherwise idle CUs take a quarter of its bytes each).
@@ -1215,6 +1219,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool
     if (head_dim == 128 && block_n == 32 && narrow && !fp8) return launch_nb<128, 1, 32>(a, false, stream);
     return hipErrorInvalidValue;
   }
+  if (head_dim == 64) return launch_d<64>(a, fp8, narrow, stream);
   if (head_dim == 128) return launch_d<128>(a, fp8, narrow, stream);
   if (head_dim == 256) return launch_d<256>(a, fp8, narrow, stream);
   return hipErrorInvalidValue;

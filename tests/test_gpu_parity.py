@@ -55,6 +55,13 @@ RANDOM_CASES = [
     (8, 32, 8, 128, 16, "fp8_e4m3", [(140, 140), (141, 9)]),
     (9, 32, 8, 128, 16, "bf16", [(4100, 12), (4096, 3), (4097, 1), (8200, 2)]),
     (10, 24, 4, 256, 16, "fp8_e4m3", [(4100, 30), (8193, 1)]),
+    # head_dim 64: persistent wide (scalar page addressing) + narrow, per-lane pow2 pages,
+    # general pages, fp8 with a split row, narrow rows spanning splits
+    (11, 16, 4, 64, 16, "bf16", [(300, 300), (301, 3), (70, 1), (129, 16), (64, 64)]),
+    (12, 16, 2, 64, 4, "bf16", [(200, 200), (201, 7), (33, 33)]),
+    (13, 16, 4, 64, 5, "bf16", [(150, 150), (151, 2)]),
+    (14, 16, 4, 64, 16, "fp8_e4m3", [(160, 160), (161, 5), (4100, 30)]),
+    (15, 32, 8, 64, 16, "bf16", [(4100, 12), (8200, 2), (4097, 1)]),
 ]
 
 

@@ -63,6 +63,8 @@ CASES = {
                                             specs=[(160, 160), (161, 5), (70, 1), (4100, 30)]), "batch"),
     "bf16_d256": lambda: (wl.random_workload(6, hq=24, hkv=4, d=256, page_size=16, kv_dtype="bf16",
                                              specs=[(160, 160), (161, 5), (70, 1)]), "batch"),
+    "bf16_d64": lambda: (wl.random_workload(11, hq=16, hkv=4, d=64, page_size=16, kv_dtype="bf16",
+                                            specs=[(300, 300), (301, 3), (70, 1), (4100, 12)]), "batch"),
 }
 
 

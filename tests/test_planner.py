@@ -297,7 +297,8 @@ def test_malformed_batches_are_rejected(dpp, mutate, status):
 
 
 @pytest.mark.parametrize("args,status", [
-    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=64), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=96), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=512), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=30, num_kv_heads=8, head_dim=128), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=-1), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1025), "DPP_ERR_UNSUPPORTED"),
