@@ -122,29 +122,23 @@ __device__ inline int chunk_off_v(int key, int c) {
   return key * ROW_BYTES + ((c ^ vswz<ROW_BYTES>(key)) << 4);
 }
 
-// OCP E4M3 code -> fp32 (exact): 1 sign, 4 exponent bits (bias 7), 3 mantissa bits,
-// S.1111.111 is NaN, no infinities.
-__device__ inline float e4m3_to_f32(uint32_t code) {
-  const uint32_t sign = (code & 0x80u) << 24;
-  const uint32_t em = code & 0x7Fu;
-  if (em == 0x7Fu) return __uint_as_float(0x7FC00000u | sign);
-  if (em < 8u) return __uint_as_float(sign | __float_as_uint((float)em * 0.001953125f));
-  return __uint_as_float(sign | ((em + (120u << 3)) << 20));
-}
-
 // Two fp32 -> two bf16, round to nearest even, in one v_cvt_pk_bf16_f32.
 __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2){lo, hi}, bf16x2));
 }
 
-// 8 E4M3 codes -> 8 bf16, value = decode(code) * scale (exact for power-of-two scales).
+// 8 OCP E4M3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa bits; S.1111.111 is NaN,
+// no infinities) -> 8 bf16, value = decode(code) * scale. v_cvt_pk_f32_fp8 decodes two codes of
+// a word exactly to fp32 (every E4M3 value is an fp32 value); the product is rounded to bf16
+// (exact for power-of-two scales).
 __device__ inline u32x4 dequant8(u32x2 raw, float scale) {
   u32x4 out;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const uint32_t x = raw[w];
-    out[2 * w] = pack_bf16x2(e4m3_to_f32(x & 0xFFu) * scale, e4m3_to_f32((x >> 8) & 0xFFu) * scale);
-    out[2 * w + 1] = pack_bf16x2(e4m3_to_f32((x >> 16) & 0xFFu) * scale, e4m3_to_f32(x >> 24) * scale);
+    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], false);  // codes in bytes 0, 1
+    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)raw[w], true);   // bytes 2, 3
+    out[2 * w] = pack_bf16x2(lo[0] * scale, lo[1] * scale);
+    out[2 * w + 1] = pack_bf16x2(hi[0] * scale, hi[1] * scale);
   }
   return out;
 }
