@@ -13,6 +13,10 @@ value     extend KV GB/s: 16 requests, each extending 1-4 tokens behind a 1024-t
           of its prefix pages and 8 such pools are rotated across steps (> 512 MB), so the
           256 MB Infinity Cache cannot serve the KV: logical KV bytes / step time.
 prefill   cold 16 x 1028-token causal prefill, same shapes: causal FLOPs / step time.
+others    the remaining configurations, each timed and its cached-vs-full bits checked: the
+          67-token prompt (full prefill vs 3-token extend, latency), the mixed batch (3,700-token
+          prefill + 7 cached tails, causal TFLOP/s) and the long fp8 path (24/4/256, 8k and 32k
+          prefills and a 1k extend behind 31k cached keys: TFLOP/s and workspace bytes).
 decode    8 one-token decodes over 8k-128k keys each (same shapes, 2-32 KV splits a row, the
           split partials merged): logical KV bytes / step time (1.4 GB of KV, far past the
           Infinity Cache).
@@ -176,6 +180,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-others", action="store_true")
     ap.add_argument("--only", choices=["extend", "prefill", "decode", "copy"], default=None,
                     help="run one leg only and print its timing (for profiler runs)")
     args = ap.parse_args()
@@ -297,6 +302,64 @@ def main() -> int:
                                 workspace=dr.plan.info.workspace_bytes)
         del dr
 
+    # ---------------------------------------------------------------- remaining configurations
+    others = {}
+    if args.only is None and not args.no_others:
+        def bits_equal(a_batch, oa, la, b_batch, ob, lb, pairs):
+            worst = 0.0
+            for ra, rb in pairs:
+                ia, ib = wl.matching_rows(a_batch, ra, b_batch, rb)
+                worst = max(worst, float((oa[ia].float() - ob[ib].float()).abs().max()),
+                            float((la[ia] - lb[ib]).abs().max()))
+            return worst
+
+        def timed_leg(work, batch, steps, warmup):
+            rr = Runner(work, batch, replicas=1)
+            o, l = rr.outputs(0)
+            ms, _ = rr.timed(steps, warmup)
+            info = rr.plan.info
+            del rr
+            return ms, o, l, info
+
+        log("single 67-token prompt")
+        w1 = wl.single_extend()
+        ms_f, o_f, l_f, _ = timed_leg(w1, w1.batches["full"], 50, 10)
+        ms_c, o_c, l_c, _ = timed_leg(w1, w1.batches["cached"], 50, 10)
+        others["single_extend_67"] = {
+            "workload": "one 67-token prompt, 32/8/128 bf16, page 16: full prefill vs 3-token extend behind 64 cached tokens",
+            "full_prefill_us": round(ms_f * 1e3, 2), "extend_us": round(ms_c * 1e3, 2),
+            "cached_vs_full_max_abs_diff": bits_equal(w1.batches["cached"], o_c, l_c, w1.batches["full"], o_f, l_f, [(0, 0)])}
+        log("mixed batch")
+        w4 = wl.mixed_batch()
+        mb, fb = w4.batches["mixed"], w4.batches["full"]
+        ms_m, o_m, l_m, info_m = timed_leg(w4, mb, 20, 20)
+        _, o_mf, l_mf, _ = timed_leg(w4, fb, 1, 1)
+        fl_m = causal_flops(mb, hq, d)
+        others["mixed_3700_plus_7_tails"] = {
+            "workload": "one 3,700-token prefill + 7 requests with 3,700 cached tokens and tails 1/2/4/6/37/64/300, 32/8/128 bf16, page 16",
+            "us_per_step": round(ms_m * 1e3, 2), "causal_flops": fl_m,
+            "tflops": round(fl_m / (ms_m * 1e-3) / 1e12, 2),
+            "cached_vs_full_max_abs_diff": bits_equal(mb, o_m, l_m, fb, o_mf, l_mf, [(i + 1, i) for i in range(7)])}
+        log("long fp8 path")
+        w5 = wl.long_fp8()
+        legs = {}
+        outs = {}
+        for name in ("prefill_8192", "prefill_32768", "extend"):
+            b5 = w5.batches[name]
+            ms5, o5, l5, info5 = timed_leg(w5, b5, 5 if name == "prefill_32768" else 10, 3)
+            fl5 = causal_flops(b5, w5.num_qo_heads, w5.head_dim)
+            legs[name] = {"us_per_step": round(ms5 * 1e3, 2), "causal_flops": fl5,
+                          "tflops": round(fl5 / (ms5 * 1e-3) / 1e12, 2),
+                          "workspace_bytes": info5.workspace_bytes, "passes": info5.num_passes}
+            outs[name] = (o5, l5)
+        legs["extend_vs_32k_prefill_max_abs_diff"] = bits_equal(
+            w5.batches["extend"], *outs["extend"], w5.batches["prefill_32768"], *outs["prefill_32768"], [(0, 0)])
+        others["long_fp8_24x4x256"] = dict(
+            workload="24 q / 4 kv heads, head_dim 256, fp8 E4M3 KV (N(0,1) x 32, scale 1/32), page 16: "
+                     "prefills of 8,192 and 32,768 tokens, a 1,024-token extend behind 31,744 cached tokens",
+            **legs)
+        del outs
+
     ext = result["extend"]
     traffic = traffic_from_profile(ext["alg_bytes"])
     line = {
@@ -358,6 +421,8 @@ def main() -> int:
                           "roofline": {"bound": "hbm", "achieved": round(dd["gbps"], 2),
                                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                                        "frac": round(dd["gbps"] / HBM_PEAK_GBPS, 4)}}
+    if others:
+        line["other_configs"] = others
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(ext["work"], ext["batch"], args.cpu_budget_s)
