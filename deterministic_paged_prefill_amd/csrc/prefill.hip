@@ -2,8 +2,8 @@
 //
 // A unit = one (q tile, KV split, kv head); a workgroup runs one unit, or in a persistent
 // launch a chain of units. Each wave owns 32 packed rows as two 16-row MFMA column blocks;
-// 8 waves (two per SIMD, 256-row tiles) at head_dim 128, 4 waves (one per SIMD, 128-row
-// tiles) at head_dim 256. Per KV tile of BN keys (64 at head_dim 128, 32 at head_dim 256;
+// 8 waves (two per SIMD, 256-row tiles) at head_dim 64 and 128, 4 waves (one per SIMD,
+// 128-row tiles) at head_dim 256. Per KV tile of BN keys (64 at head_dim 128, 32 at head_dim 256;
 // tiles start at absolute multiples of BN):
 //   gather   16-byte chunks of K and V rows come through the page table straight into a ring
 //            of four K and four V LDS buffers by LDS-DMA, several tiles ahead (natural
@@ -1186,8 +1186,9 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
     if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
   } else if constexpr (waves_for(D) == 8 && D >= 128) {
     // A narrow launch of at most one unit per two compute units splits head_dim in PV over
-    // two workgroups per unit (same bits; a unit streams K/V at the rate one CU sustains, so
-    // the otherwise idle CUs take a quarter of its bytes each).
+    // two workgroups per unit (same bits). A CU streams a unit's gather at a rate of its own,
+    // so two CUs that each load all of K and half of V (3/4 of the unit's bytes) finish sooner
+    // than one that loads all of it, while the K they share comes from HBM once.
     if (2 * a.num_items * a.num_kv_heads <= compute_units()) {
       return pow2 && P <= BNX ? launch_one<D, false, NB, kPagesPow2, true, BNX>(a, stream)
                               : launch_one<D, false, NB, kPagesGeneral, true, BNX>(a, stream);
