@@ -440,3 +440,26 @@ def test_plan_create_ex_rejects_unknown_flags(dpp):
     st = lib.dpp_plan_create_ex(ctypes.byref(cfg), 1, b.qo_indptr.ctypes.data, b.kv_indptr.ctypes.data,
                                 b.kv_last_page_len.ctypes.data, 0, 2, ctypes.byref(h))
     assert st == dpp.DPP_ERR_INVALID and h.value is None
+
+
+@pytest.mark.parametrize("specs", [[(1028, 1028)] * 2, [(1025, 1), (4100, 12), (8200, 2)]])
+def test_head_dim_64_plans_like_128(dpp, specs):
+    """head_dim 64 uses the tile of head_dim <= 128 (256 packed rows x 64 keys): the same
+    items as a head_dim 128 plan of the batch, every needed (row, split) covered, a persistent
+    unit record per (item, kv head) for wide passes, partial slots of (64 + 1) floats."""
+    b = _specs_batch(specs)
+    p64, p128 = _plan(dpp, b, d=64), _plan(dpp, b, d=128)
+    assert (p64.info.block_m, p64.info.block_n) == (256, 64) == dpp.tile_shape(64)
+    a, c = parse(p64.header()), parse(p128.header())
+    assert (a.items[:, :7] == c.items[:, :7]).all() and (a.merges == c.merges).all()
+    assert len(a.units) == len(c.units)
+    cov = _coverage(a, 4, 256)
+    for r, (kv, qlen) in enumerate(specs):
+        for R in range(qlen * 4):
+            pos = kv - qlen + R // 4
+            for s in range(pos // 4096 + 1):
+                assert (r, R, s) in cov
+    slots = p64.info.max_partial_slots
+    assert slots == p128.info.max_partial_slots
+    if slots:
+        assert p64.workspace_bytes - p64.info.header_bytes == _align(slots * 64 * 4) + _align(slots * 4)
