@@ -129,6 +129,32 @@ class Runner:
         wall_ms = (time.perf_counter() - t0) * 1e3
         return start.elapsed_time(end) / steps, wall_ms / steps
 
+    def graph_timed(self, steps_per_graph: int, replays: int):
+        """The same steps captured in one HIP graph (torch.cuda.graph over dpp_run, work list
+        uploaded beforehand) and replayed: ms per step."""
+        import torch
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=side):
+            for i in range(steps_per_graph):
+                args = list(self.args[i % self.replicas])
+                args[-1] = side.cuda_stream
+                st = self.lib.dpp_run(*args)
+                if st != 0:
+                    self.dpp._check(st)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            g.replay()
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record()
+        for _ in range(replays):
+            g.replay()
+        end.record()
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / (replays * steps_per_graph)
+
     def outputs(self, replica: int = 0):
         import torch
         self.step(replica)
@@ -237,12 +263,13 @@ def main() -> int:
         del fr
         log(f"cached-vs-full max|diff| = {max_diff}")
         ms, wall = run.timed(args.steps, args.warmup)
+        ms_graph = run.graph_timed(40, 10)
         nbytes = kv_bytes(cached, hkv, d, 2)
         io_bytes = (2 * cached.num_q_tokens * hq * d * 2 + cached.num_q_tokens * hq * 4
                     + cached.kv_indices.size * 4)
         alg = nbytes + io_bytes
         achieved = alg / (ms * 1e-3) / 1e9
-        result["extend"] = dict(ms=ms, wall_ms=wall, kv_bytes=nbytes, alg_bytes=alg, gbps=nbytes / (ms * 1e-3) / 1e9,
+        result["extend"] = dict(ms=ms, wall_ms=wall, graph_ms=ms_graph, kv_bytes=nbytes, alg_bytes=alg, gbps=nbytes / (ms * 1e-3) / 1e9,
                                 achieved=achieved, plan_us=run.plan_us, upload_us=run.upload_us,
                                 max_diff=max_diff, work=work, batch=cached,
                                 items=run.plan.info.num_prefill_items)
@@ -387,6 +414,7 @@ def main() -> int:
                      "traffic": None if traffic is None else round(traffic)},
         "extend_detail": {"us_per_step": round(ext["ms"] * 1e3, 2),
                           "host_wall_us_per_step": round(ext["wall_ms"] * 1e3, 2),
+                          "graph_replay_us_per_step": round(ext["graph_ms"] * 1e3, 2),
                           "algorithmic_bytes_per_launch": ext["alg_bytes"],
                           "work_items": ext["items"], "plan_us": round(ext["plan_us"], 1),
                           "upload_us": round(ext["upload_us"], 1),
