@@ -62,6 +62,9 @@ RANDOM_CASES = [
     (13, 16, 4, 64, 5, "bf16", [(150, 150), (151, 2)]),
     (14, 16, 4, 64, 16, "fp8_e4m3", [(160, 160), (161, 5), (4100, 30)]),
     (15, 32, 8, 64, 16, "bf16", [(4100, 12), (8200, 2), (4097, 1)]),
+    # the largest page size (one page holds a whole short prompt) and a 32-wide GQA group
+    (16, 32, 8, 128, 1024, "bf16", [(3000, 3000), (3001, 5), (1025, 1), (1024, 2)]),
+    (17, 64, 2, 128, 16, "bf16", [(200, 200), (201, 3), (33, 1)]),
 ]
 
 
