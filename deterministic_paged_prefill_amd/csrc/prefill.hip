@@ -407,6 +407,28 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       }
     }
   };
+  // Q of another unit of the chain (a persistent workgroup loads the next unit's Q during its
+  // current unit's last A phase, once the last QK^T has read the registers)
+  auto load_q_of = [&](const UnitRecord& u) {
+    const int u_rows = min(C::PLAN_BM, u.req.qo_len * g - u.row_start);
+    const bool w_rows = row_wave * C::RPW < u_rows;  // has_rows of that unit
+#pragma unroll
+    for (int nb = 0; nb < NB; ++nb) {
+      const int lr = row_wave * C::RPW + nb * 16 + li;
+      const bool valid = lr < u_rows && w_rows;
+      const int R = u.row_start + lr;
+      const int token = R / g;
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
+                           ((int64_t)(u.req.q_start + token) * a.num_qo_heads + u.kv_head * g + (R - token * g)) * D +
+                           8 * lg;
+#pragma unroll
+      for (int dc = 0; dc < C::DC; ++dc) {
+        u32x4 v = u32x4{0u, 0u, 0u, 0u};
+        if (valid) v = *reinterpret_cast<const u32x4*>(qp + dc * 32);
+        qreg[nb][dc] = __builtin_bit_cast(bf16x8, v);
+      }
+    }
+  };
   if constexpr (!kPP) {
     load_q();
     // Q and the page ids in registers and LDS before any DMA load of K or V is issued: a wait
@@ -1033,6 +1055,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     // register still being loaded needs a wait of its own.
     int32_t rcur = rv, rnext = 0, rfetch = 0;
     bool has_prev = false, rotate = false;
+    bool q_ready = false;  // this unit's Q was loaded in the previous unit's last A phase
     if (cur_next >= 0) rnext = fetch_record(cur_next);
     wait_vmcnt<0>();
     __syncthreads();  // the first unit's page ids visible
@@ -1040,8 +1063,10 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     constexpr int kEvery = (C::KC * C::DB) / kLoads;
     static_assert(kEvery >= 1, "one load per PV step at most");
     for (;;) {
-      // Q and load group -3 (K(0)); the trailing waves' rows of the previous unit
-      load_q();
+      // Q (unless loaded ahead) and load group -3 (K(0)); the trailing waves' rows of the
+      // previous unit. The full wait below covers Q either way.
+      if (!q_ready) load_q();
+      q_ready = false;
       if constexpr (MODE == kPagesScalar) {
         read_ids(-3);
         issue_group_scalar(-3);
@@ -1099,6 +1124,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
           if (has_rows) pv_acc(pb, t, no_hook);
         }
         if (has_rows && t + 1 < n_tiles) qk(s, t + 1);
+        if (t == n_tiles - 1 && has_next) {
+          // The last QK^T of this unit ran in A(t-1): its Q registers take the next unit's
+          // Q now, in flight during the output write and the transition.
+          load_q_of(decode(rnext));
+          q_ready = true;
+        }
         if (!leading) wait_vmcnt<2 * kGroupLoads>();  // group t-1, for the leading group's A(t+1)
         __syncthreads();
       }
