@@ -71,9 +71,16 @@ int oracle_num_threads(void) {
 #endif
 }
 
+/* E4M3 values of all 256 codes, filled once from oracle_e4m3_to_double (the same decode,
+ * looked up instead of recomputed per element). */
+static double g_e4m3[256];
+static void fill_e4m3_table(void) {
+  for (int c = 0; c < 256; ++c) g_e4m3[c] = oracle_e4m3_to_double((uint8_t)c);
+}
+
 static double load_kv(const void* pool, int kv_dtype, int64_t idx, double scale) {
   if (kv_dtype == 0) return oracle_bf16_to_double(((const uint16_t*)pool)[idx]);
-  return oracle_e4m3_to_double(((const uint8_t*)pool)[idx]) * scale;
+  return g_e4m3[((const uint8_t*)pool)[idx]] * scale;
 }
 
 /* Index of the request owning global query token t (qo_indptr is non-decreasing). */
@@ -128,6 +135,7 @@ int oracle_paged_prefill(int32_t batch, int32_t hq, int32_t hkv, int32_t d, int3
     if (qo_len > kv_len) return ORACLE_EINVAL;
     if (kv_len > max_kv) max_kv = kv_len;
   }
+  fill_e4m3_table();
   const int64_t nq = qo_indptr[batch];
   const int64_t n_rows = sel ? n_sel : nq;
   const int group = hq / hkv;

@@ -31,6 +31,8 @@ def _brute_force_rows(work, batch):
     outs, lses = [], []
     d = work.head_dim
     for r in batch.requests:
+        if r.qo_len == 0:
+            continue  # no rows
         q, k, v = _dense_inputs(work.prompts[r.prompt], r.kv_len)
         pos = np.arange(r.kv_len - r.qo_len, r.kv_len)
         o, lse = wl_dense(q[pos], k, v, pos, 1.0 / math.sqrt(d))
@@ -264,3 +266,37 @@ def test_e4m3_decode_all_codes(oracle_lib):
     assert table[0x7E] == 448.0 and table[0xFE] == -448.0       # largest finite
     assert table[0x01] == 2.0 ** -9 and table[0x08] == 2.0 ** -6  # min subnormal / normal
     assert table[0x38] == 1.0 and table[0x80] == 0.0 and math.copysign(1, table[0x80]) < 0
+
+
+@pytest.mark.parametrize("page", [1, 4, 16])
+def test_row_subset_equals_brute_force_rows(oracle_lib, page):
+    """The rows= path (what every large GPU check uses): any selection of global query tokens,
+    unsorted and with repeats, around zero-length requests, gives exactly the rows of the full
+    run and matches the numpy brute force row by row."""
+    specs = [(5, 0), (9, 4), (0, 0), (23, 23), (16, 0), (40, 17), (1, 1), (0, 0), (12, 3)]
+    work = wl.random_workload(41 + page, hq=6, hkv=2, d=16, page_size=page, kv_dtype="bf16",
+                              specs=specs)
+    batch = work.batches["batch"]
+    kw = work.oracle_kwargs(batch)
+    o_all, l_all = oracle_lib.paged_prefill(**kw)
+    o_bf, l_bf = _brute_force_rows(work, batch)
+    nq = batch.num_q_tokens
+    rng = np.random.default_rng(page)
+    # every request's first and last row (their starts coincide with empty requests' starts)
+    edges = []
+    for r in range(batch.batch_size):
+        a, b = int(batch.qo_indptr[r]), int(batch.qo_indptr[r + 1])
+        if b > a:
+            edges += [a, b - 1]
+    rows = np.concatenate([rng.permutation(nq), np.array(edges[::-1]), rng.integers(0, nq, 7)])
+    o, lse = oracle_lib.paged_prefill(**kw, rows=rows)
+    assert o.shape == (len(rows), 6, 16)
+    np.testing.assert_array_equal(o, o_all[rows])
+    np.testing.assert_array_equal(lse, l_all[rows])
+    np.testing.assert_allclose(o, o_bf[rows], rtol=0, atol=1e-12)
+    np.testing.assert_allclose(lse, l_bf[rows], rtol=0, atol=1e-12)
+    # an empty selection and a selection outside the batch
+    o0, l0 = oracle_lib.paged_prefill(**kw, rows=[])
+    assert o0.shape == (0, 6, 16) and l0.shape == (0, 6)
+    with pytest.raises(ValueError):
+        oracle_lib.paged_prefill(**kw, rows=[nq])
