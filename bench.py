@@ -105,7 +105,7 @@ class Runner:
         self.upload_us = (time.perf_counter() - t0) * 1e6
         self.replicas = replicas
         self.args = [(self.plan._h, self.q.data_ptr(), self.q.shape[0], self.k.data_ptr(),
-                      self.v.data_ptr(), self.k.shape[0], kvi.data_ptr(), self.o.data_ptr(),
+                      self.v.data_ptr(), self.k.shape[0], kvi.data_ptr(), kvi.numel(), self.o.data_ptr(),
                       self.lse.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
                       dpp.RUN_REUSE_UPLOAD, self.stream.cuda_stream) for kvi in self.kvi]
 

@@ -18,7 +18,6 @@ Importing the package does not load the library; the first call does, and raises
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -39,6 +38,7 @@ def tile_shape(head_dim: int) -> tuple:
 DPP_OK, DPP_ERR_INVALID, DPP_ERR_SHAPE, DPP_ERR_UNSUPPORTED, DPP_ERR_WORKSPACE, DPP_ERR_HIP = range(6)
 RUN_REUSE_UPLOAD = 1
 PLAN_ADAPTIVE_KV_TILE = 1  # comparison mode: NOT batch invariant (see include/dpp.h)
+PLAN_PERMUTE_WORK = 2      # test mode: work order shuffled with the seed in bits 16..31
 KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}
 
 
@@ -87,8 +87,8 @@ class PlanInfo:
 
 _lib = None
 EXPORTS = ("dpp_plan_create", "dpp_plan_create_ex", "dpp_plan_workspace_bytes", "dpp_plan_get_info", "dpp_plan_header",
-           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_merge_states", "dpp_last_error",
-           "dpp_status_string", "dpp_abi_version")
+           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_check_page_table", "dpp_merge_states",
+           "dpp_last_error", "dpp_status_string", "dpp_abi_version")
 
 
 def library():
@@ -117,7 +117,9 @@ def library():
     lib.dpp_plan_destroy.restype = None
     lib.dpp_plan_destroy.argtypes = [vp]
     lib.dpp_run.restype = ctypes.c_int
-    lib.dpp_run.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, vp, vp, sz, ctypes.c_uint32, vp]
+    lib.dpp_run.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, sz, ctypes.c_uint32, vp]
+    lib.dpp_check_page_table.restype = ctypes.c_int
+    lib.dpp_check_page_table.argtypes = [vp, vp, i64, i64]
     lib.dpp_merge_states.restype = ctypes.c_int
     lib.dpp_merge_states.argtypes = [vp, vp, i64, i32, i32, i32, vp, vp, vp]
     lib.dpp_last_error.restype = ctypes.c_char_p
@@ -238,8 +240,14 @@ class Plan:
             if reuse_upload:
                 raise ValueError("reuse_upload needs the workspace the plan was uploaded to")
             workspace = self.new_workspace(q.device)
+            if stream is not None and _stream_handle(stream) != torch.cuda.current_stream(q.device).cuda_stream:
+                # allocated on the current stream, used on `stream`: keep the caching
+                # allocator from handing it out again before that stream's kernels are done
+                workspace.record_stream(stream if isinstance(stream, torch.cuda.Stream)
+                                        else torch.cuda.ExternalStream(_stream_handle(stream)))
         status = library().dpp_run(self._h, q.data_ptr(), rows, k_pool.data_ptr(), v_pool.data_ptr(),
-                                   k_pool.shape[0], None if ragged else kv_indices.data_ptr(), out.data_ptr(),
+                                   k_pool.shape[0], None if ragged else kv_indices.data_ptr(),
+                                   0 if ragged else kv_indices.numel(), out.data_ptr(),
                                    lse.data_ptr(), workspace.data_ptr(),
                                    workspace.numel() * workspace.element_size(),
                                    RUN_REUSE_UPLOAD if reuse_upload else 0,
@@ -247,6 +255,13 @@ class Plan:
         _check(status)
         self._ran = True
         return out, lse
+
+    def check_page_table(self, kv_indices, num_pages: int) -> None:
+        """Host check that every page id the plan's requests read lies in [0, num_pages)
+        (dpp_check_page_table); raises DppValueError naming the first bad (request, page)."""
+        kvi = _i32(kv_indices)
+        _check(library().dpp_check_page_table(self._h, kvi.ctypes.data if kvi.size else None,
+                                              kvi.size, int(num_pages)))
 
     def close(self) -> None:
         if self._h is not None:
@@ -266,11 +281,14 @@ class Plan:
 def plan(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, qo_indptr,
          kv_indptr, kv_last_page_len=None, *, kv_dtype: str = "bf16", sm_scale: float | None = None,
          k_scale: float = 1.0, v_scale: float = 1.0,
-         workspace_cap: int = DEFAULT_WORKSPACE_CAP, adaptive_kv_tile: bool = False) -> Plan:
+         workspace_cap: int = DEFAULT_WORKSPACE_CAP, adaptive_kv_tile: bool = False,
+         permute_seed: int | None = None) -> Plan:
     """Plan one batch from host copies of its index arrays (no GPU work).
 
     ``adaptive_kv_tile=True`` is the comparison mode that picks the KV tile from the batch
-    (dpp_plan_create_ex with DPP_PLAN_ADAPTIVE_KV_TILE): NOT batch invariant."""
+    (dpp_plan_create_ex with DPP_PLAN_ADAPTIVE_KV_TILE): NOT batch invariant.
+    ``permute_seed`` (test mode, DPP_PLAN_PERMUTE_WORK) shuffles the order of the work in every
+    pass; the results stay bit-identical."""
     if kv_dtype not in KV_DTYPES:
         raise ValueError(f"kv_dtype must be one of {sorted(KV_DTYPES)}")
     qo, kvp = _i32(qo_indptr), _i32(kv_indptr)
@@ -288,7 +306,9 @@ def plan(num_qo_heads: int, num_kv_heads: int, head_dim: int, page_size: int, qo
     last_ptr = last.ctypes.data if batch > 0 else None
     _check(library().dpp_plan_create_ex(ctypes.byref(cfg), batch, qo.ctypes.data, kvp.ctypes.data,
                                         last_ptr, int(workspace_cap),
-                                        PLAN_ADAPTIVE_KV_TILE if adaptive_kv_tile else 0,
+                                        (PLAN_ADAPTIVE_KV_TILE if adaptive_kv_tile else 0) |
+                                        (0 if permute_seed is None else
+                                         PLAN_PERMUTE_WORK | ((int(permute_seed) & 0xFFFF) << 16)),
                                         ctypes.byref(h)))
     return Plan(h, cfg, batch)
 
@@ -312,6 +332,3 @@ def merge_states(o_partial, lse_partial, out=None, lse=None, stream=None):
                                       out.data_ptr(), lse.data_ptr(), _stream_handle(stream)))
     return out, lse
 
-
-def default_sm_scale(head_dim: int) -> float:
-    return 1.0 / math.sqrt(head_dim)

@@ -56,6 +56,19 @@ dpp_status enqueue_upload(const dpp_plan* plan, void* workspace, hipStream_t str
   }
   hipError_t e = hipMemcpyAsync(workspace, plan->pinned, hbytes, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_fail(e, "hipMemcpyAsync(work list)");
+  std::lock_guard<std::mutex> lock(plan->pinned_mu);
+  plan->uploaded_ws = workspace;
+  return DPP_OK;
+}
+
+// A run that reuses an upload must name the workspace that upload went to: otherwise the
+// kernels would find another plan's work list (or none) and write nothing.
+dpp_status check_reuse(const dpp_plan* plan, const void* workspace) {
+  std::lock_guard<std::mutex> lock(plan->pinned_mu);
+  if (plan->uploaded_ws != workspace)
+    return fail(DPP_ERR_INVALID, plan->uploaded_ws ? "DPP_RUN_REUSE_UPLOAD: this plan's work list was uploaded to "
+                                                     "another workspace"
+                                                   : "DPP_RUN_REUSE_UPLOAD: this plan was never uploaded");
   return DPP_OK;
 }
 
@@ -71,8 +84,8 @@ extern "C" dpp_status dpp_plan_upload(const dpp_plan* plan, void* workspace, siz
 
 extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows,
                               const void* k_pool, const void* v_pool, int64_t num_pages,
-                              const int32_t* kv_indices, void* o, float* lse, void* workspace,
-                              size_t workspace_bytes, uint32_t flags, void* stream_ptr) {
+                              const int32_t* kv_indices, int64_t num_kv_indices, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream_ptr) {
   if (!plan) return fail(DPP_ERR_INVALID, "dpp_run: null plan");
   if (q_rows != plan->total_q_rows)
     return fail(DPP_ERR_SHAPE, "q has " + std::to_string(q_rows) + " rows but qo_indptr[-1] is " +
@@ -90,15 +103,21 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
   if (plan->ragged && plan->total_kv_tokens > num_pages)
     return fail(DPP_ERR_SHAPE, "ragged KV: kv_indptr[-1] = " + std::to_string(plan->total_kv_tokens) +
                                    " tokens but k/v hold " + std::to_string(num_pages));
+  // paged KV: the kernels read kv_indices[kv_indptr[r] ..) for every request
+  if (!plan->ragged && plan->total_kv_entries > num_kv_indices)
+    return fail(DPP_ERR_SHAPE, "kv_indices holds " + std::to_string(num_kv_indices) +
+                                   " page ids but kv_indptr[-1] is " + std::to_string(plan->total_kv_entries));
   if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(lse, 4) || (!plan->ragged && !aligned(kv_indices, 4)))
     return fail(DPP_ERR_INVALID, "dpp_run: q/o/k_pool/v_pool must be 16-byte aligned");
   hipStream_t stream = (hipStream_t)stream_ptr;
   if (plan->num_items == 0) return DPP_OK;
-  if (!(flags & DPP_RUN_REUSE_UPLOAD)) {
+  if (flags & DPP_RUN_REUSE_UPLOAD) {
+    st = check_reuse(plan, workspace);
+  } else {
     st = enqueue_upload(plan, workspace, stream);
-    if (st != DPP_OK) return st;
   }
+  if (st != DPP_OK) return st;
   hipError_t e;
 
   char* ws = (char*)workspace;
@@ -155,6 +174,31 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
     if (m.num_merges > 0) {
       e = launch_merge(m, plan->cfg.head_dim, plan->cfg.num_kv_heads, stream);
       if (e != hipSuccess) return hip_fail(e, "merge launch");
+    }
+  }
+  return DPP_OK;
+}
+
+extern "C" dpp_status dpp_check_page_table(const dpp_plan* plan, const int32_t* kv_indices_host,
+                                           int64_t num_kv_indices, int64_t num_pages) {
+  if (!plan) return fail(DPP_ERR_INVALID, "dpp_check_page_table: null plan");
+  if (num_pages < 0 || num_kv_indices < 0) return fail(DPP_ERR_INVALID, "dpp_check_page_table: negative count");
+  if (plan->ragged) return DPP_OK;  // no page table
+  if (plan->total_kv_entries > num_kv_indices)
+    return fail(DPP_ERR_SHAPE, "kv_indices holds " + std::to_string(num_kv_indices) +
+                                   " page ids but kv_indptr[-1] is " + std::to_string(plan->total_kv_entries));
+  if (plan->total_kv_entries > 0 && !kv_indices_host) return fail(DPP_ERR_INVALID, "dpp_check_page_table: null kv_indices");
+  // every page a request reads: ceil(kv_len / page_size) ids from its page_start
+  const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(plan->header.data());
+  const RequestDesc* reqs = reinterpret_cast<const RequestDesc*>(plan->header.data() + pre->request_offset);
+  const int64_t P = plan->cfg.page_size;
+  for (int32_t r = 0; r < plan->batch_size; ++r) {
+    const int64_t n = (reqs[r].kv_len + P - 1) / P;
+    for (int64_t j = 0; j < n; ++j) {
+      const int64_t id = kv_indices_host[reqs[r].page_start + j];
+      if (id < 0 || id >= num_pages)
+        return fail(DPP_ERR_SHAPE, "request " + std::to_string(r) + ", page " + std::to_string(j) + ": id " +
+                                       std::to_string(id) + " outside [0, " + std::to_string(num_pages) + ")");
     }
   }
   return DPP_OK;

@@ -102,7 +102,7 @@ struct PrefillItem {
   int32_t kv_tile_begin; // first KV tile (absolute, units of block_n_for(head_dim))
   int32_t kv_tile_end;   // one past the last KV tile this item visits
   int32_t slot_base;     // first partial slot of the tile in this pass, -1 if S_t == 1
-  int32_t pad0;
+  int32_t pass;          // the pass (launch group) that runs the item; the kernels ignore it
   RequestDesc req;       // the request's descriptor
   int32_t pad1[4];
 };

@@ -89,6 +89,7 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
   if (pre->magic != kHeaderMagic || pre->plan_id != a.plan_id) return;  // not this plan's work list
   const MergeItem mi = reinterpret_cast<const MergeItem*>(a.header + pre->merge_offset)[a.merge_begin + blockIdx.x];
+  if (mi.tile_splits < 2 || mi.slot_base < 0) return;  // no slot block: nothing was written for it
   const RequestDesc rq = reinterpret_cast<const RequestDesc*>(a.header + pre->request_offset)[mi.request];
   const int kvh = blockIdx.y;
   const int g = a.group;

@@ -145,8 +145,10 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
                                          const int32_t* last_page_len, size_t workspace_cap,
                                          uint32_t plan_flags, dpp_plan** out_plan) {
   if (out_plan) *out_plan = nullptr;
-  if (plan_flags & ~(uint32_t)DPP_PLAN_ADAPTIVE_KV_TILE)
+  if (plan_flags & ~(uint32_t)(DPP_PLAN_ADAPTIVE_KV_TILE | DPP_PLAN_PERMUTE_WORK | DPP_PLAN_PERMUTE_SEED(0xFFFF)))
     return fail(DPP_ERR_INVALID, "dpp_plan_create_ex: unknown plan flags");
+  if (!(plan_flags & DPP_PLAN_PERMUTE_WORK) && (plan_flags >> 16))
+    return fail(DPP_ERR_INVALID, "dpp_plan_create_ex: a permutation seed without DPP_PLAN_PERMUTE_WORK");
   if (!cfg || !out_plan) return fail(DPP_ERR_INVALID, "dpp_plan_create: null cfg or out_plan");
   if (batch_size < 0) return fail(DPP_ERR_INVALID, "dpp_plan_create: negative batch_size");
   const bool ragged = cfg && cfg->page_size == 0;
@@ -320,6 +322,7 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
         it.kv_tile_begin = s * tiles_per_split;
         it.kv_tile_end = (int32_t)std::min<int64_t>((int64_t)(s + 1) * tiles_per_split, last_tile + 1);
         it.slot_base = (int32_t)t.slot_base;
+        it.pass = p;
         it.req = rq;
         const int64_t key_lo = (int64_t)it.kv_tile_begin * block_n;
         const int64_t key_hi = std::min<int64_t>((int64_t)it.kv_tile_end * block_n, rq.kv_len);
@@ -343,6 +346,20 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
                        if (a.request != b.request) return a.request < b.request;
                        return (a.kv_tile_end - a.kv_tile_begin) > (b.kv_tile_end - b.kv_tile_begin);
                      });
+    if (plan_flags & DPP_PLAN_PERMUTE_WORK) {
+      // test mode: any order of the pass's work must give the same bits
+      uint64_t st = 0x9E3779B97F4A7C15ull ^ ((uint64_t)(plan_flags >> 16) << 32) ^ (uint64_t)p;
+      auto next = [&](uint64_t n) {  // splitmix64, reduced to [0, n)
+        st += 0x9E3779B97F4A7C15ull;
+        uint64_t z = st;
+        z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+        z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+        return (z ^ (z >> 31)) % n;
+      };
+      for (size_t k = items.size() - first; k > 1; --k) std::swap(items[first + k - 1], items[first + next(k)]);
+      const size_t mfirst = (size_t)plan->merge_pass.back();  // this pass's first merge
+      for (size_t k = merges.size() - mfirst; k > 1; --k) std::swap(merges[mfirst + k - 1], merges[mfirst + next(k)]);
+    }
     // A pass whose tiles all have at most kNarrowRows rows (extends) runs on the narrow
     // kernel; a pass with wider tiles runs all its items in one launch of the wide kernel,
     // so that its short tiles fill in behind the long ones instead of running after them.
@@ -414,6 +431,7 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
   plan->ragged = ragged;
   plan->block_n = block_n;
   plan->total_kv_tokens = ragged && batch_size > 0 ? kv_indptr[batch_size] : 0;
+  plan->total_kv_entries = batch_size > 0 ? kv_indptr[batch_size] : 0;
   *out_plan = plan.release();
   return DPP_OK;
 }
@@ -458,4 +476,4 @@ extern "C" const char* dpp_status_string(dpp_status st) {
   return "DPP_ERR_UNKNOWN";
 }
 
-extern "C" int32_t dpp_abi_version(void) { return 2; }
+extern "C" int32_t dpp_abi_version(void) { return 3; }

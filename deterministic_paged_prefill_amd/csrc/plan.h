@@ -44,12 +44,17 @@ struct dpp_plan {
   int32_t block_n = 0;            // keys per KV tile: block_n_for(head_dim), except in the
                                   // adaptive-tile comparison mode
   int64_t total_kv_tokens = 0;    // ragged: kv_indptr[B], the KV rows the kernels may read
+  int64_t total_kv_entries = 0;   // kv_indptr[B]: page ids the kernels read from kv_indices
+                                  // (paged), or KV token rows (ragged)
   int32_t item_offset = 0;        // word offset of the item records in the header
   uint32_t plan_id = 0;           // stamped into the work list
 
   // Pinned host copy of `header`, created on first dpp_run (plan creation stays HIP-free).
   mutable std::mutex pinned_mu;
   mutable void* pinned = nullptr;
+  // Workspace of the last enqueued upload of this plan's work list (guarded by pinned_mu):
+  // a run that reuses an upload must name the same workspace.
+  mutable const void* uploaded_ws = nullptr;
 };
 
 namespace dpp {

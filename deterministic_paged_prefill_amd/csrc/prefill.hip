@@ -720,8 +720,11 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
                 u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
                       pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
         }
-      } else if (mine) {
-        // a row reaching past the first split: its fp32 partial, straight from the MFMA layout
+      } else if (mine && e.tile_splits > 1 && e.slot_base >= 0) {
+        // a row reaching past the first split: its fp32 partial, straight from the MFMA layout.
+        // Only a tile whose last row needs several splits owns a slot block (slot_base >= 0);
+        // the planner guarantees p >= 4096 implies that, and the test keeps a slip from writing
+        // below the partial region.
         const int64_t slot = partial_slot(e.slot_base, e.tile_splits, e.kv_head, e.split, lr, slot_rows_for(e_rows));
         DPP_GLOBAL float* pp = part_o_out + slot * D + vh * (D / 2) + 4 * lg;
 #pragma unroll

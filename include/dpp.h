@@ -105,6 +105,13 @@ typedef struct {
 /*
  * Build the plan of one batch. Host only: no HIP call, no device memory.
  *
+ * Defining passages: a paged prefill wrapper planned on the host from the batch's index
+ * arrays, probed cold and on a radix hit (sglang PR #46351 page, "Validation"; its host-plan
+ * test suite under "Tests"); what the plan may not do is size its q tile from the batch
+ * ("Root cause"); its fixed 4096-token KV splits and the bounded
+ * partial buffer they need come from the model-serving-minefield issue #73 correction comment
+ * ("What the flag actually does", item 2, and "The failure").
+ *
  *   cfg                  model constants (copied)
  *   batch_size           B >= 0
  *   qo_indptr_host       [B+1] int32, qo_indptr[0] == 0, non-decreasing
@@ -128,6 +135,12 @@ dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
 
 /* dpp_plan_create_ex flags */
 #define DPP_PLAN_ADAPTIVE_KV_TILE 1u
+/* Test mode: shuffle the order of the work inside every pass (items, merges, and hence the
+ * workgroup and persistent chain each unit lands in) with the seed in bits 16..31 of the
+ * flags. Results must not change by a bit: the pages find the reduction order batch
+ * invariant once the tile is fixed (sglang PR #46351 page, "Root cause"). */
+#define DPP_PLAN_PERMUTE_WORK 2u
+#define DPP_PLAN_PERMUTE_SEED(seed) (((uint32_t)(seed) & 0xFFFFu) << 16)
 
 /*
  * dpp_plan_create with plan flags (0: identical to dpp_plan_create). DPP_PLAN_ADAPTIVE_KV_TILE
@@ -138,6 +151,8 @@ dpp_status dpp_plan_create(const dpp_config* cfg, int32_t batch_size,
  * 32-key KV tiles at head_dim 128 (bf16) instead of 64. Such a batch's rows then differ in
  * their last bits from the same rows planned in a larger batch; it exists to measure that
  * difference and what the fixed tile costs. dpp_plan_info.block_n reports the tile used.
+ * DPP_PLAN_PERMUTE_WORK (with DPP_PLAN_PERMUTE_SEED) only reorders work; a test compares its
+ * results with the default plan's bit for bit.
  * Errors: those of dpp_plan_create, and DPP_ERR_INVALID for unknown flag bits.
  */
 dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_size,
@@ -176,28 +191,56 @@ void dpp_plan_destroy(dpp_plan* plan);
 /*
  * Run the planned attention on `stream` (a hipStream_t; NULL = the null stream).
  *
+ * Defining passages: the operation at the top of this header (sglang PR #46351 page,
+ * "Motivation" and "Fix"); the shape check that q holds qo_indptr[-1] rows is the one that
+ * page's Woody-Hu report shows FlashInfer raising as a ValueError; a workspace too small for
+ * the plan is refused before any launch, the opposite of the overflow in the
+ * model-serving-minefield issue #73 correction comment ("The failure").
+ *
  *   q, k_pool, v_pool, kv_indices, o, lse   device pointers, layouts above
  *   q_rows        rows of q and o; must equal qo_indptr[B] of the plan (DPP_ERR_SHAPE)
- *   num_pages     pages in each pool; a page id outside [0, num_pages) reads as zeros. Ragged
- *                 KV: the token rows of k_pool / v_pool; kv_indptr[B] above it is
- *                 DPP_ERR_SHAPE, and kv_indices may be NULL
+ *   num_pages     pages in each pool. Page ids are the caller's contract: every id a request
+ *                 reads must lie in [0, num_pages) (dpp_check_page_table checks a host copy);
+ *                 the kernels never read outside the pools, and an id outside that range
+ *                 reads as zeros. Ragged KV: the token rows of k_pool / v_pool; kv_indptr[B]
+ *                 above it is DPP_ERR_SHAPE, and kv_indices may be NULL
+ *   num_kv_indices  entries of kv_indices; below kv_indptr[B] of the plan is DPP_ERR_SHAPE
+ *                 (ignored for ragged KV)
  *   workspace     device buffer of at least dpp_plan_workspace_bytes(plan) bytes, 256-byte
  *                 aligned; its contents are scratch (work list + split partials)
  *   flags         0, or DPP_RUN_REUSE_UPLOAD when dpp_plan_upload (or an earlier dpp_run) has
- *                 already put this plan's work list into this workspace on this stream
+ *                 already put this plan's work list into this workspace on this stream. The
+ *                 plan remembers the workspace of its last upload: reusing an upload with any
+ *                 other workspace (or with none made) is DPP_ERR_INVALID. Writing over the
+ *                 head of the workspace between the upload and the run is the caller's fault:
+ *                 the kernels then find no work list of this plan and write nothing
  *
  * Enqueues: the async copy of the work list into the workspace (unless reused), then per pass
  * one prefill launch and (if some row spans several splits) one merge launch. Returns without
  * waiting.
- * On DPP_ERR_SHAPE / DPP_ERR_WORKSPACE / DPP_ERR_UNSUPPORTED nothing is enqueued.
+ * On DPP_ERR_INVALID / DPP_ERR_SHAPE / DPP_ERR_WORKSPACE / DPP_ERR_UNSUPPORTED nothing is
+ * enqueued.
  */
 dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows, const void* k_pool,
-                   const void* v_pool, int64_t num_pages, const int32_t* kv_indices, void* o,
-                   float* lse, void* workspace, size_t workspace_bytes, uint32_t flags,
-                   void* stream);
+                   const void* v_pool, int64_t num_pages, const int32_t* kv_indices,
+                   int64_t num_kv_indices, void* o, float* lse, void* workspace,
+                   size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * Host check of a page table against a plan: kv_indices_host holds at least kv_indptr[B]
+ * entries and every page id that a request of the plan reads lies in [0, num_pages).
+ * DPP_ERR_SHAPE names the first offending (request, page); DPP_ERR_INVALID on null or
+ * negative arguments. A ragged plan has no page table: DPP_OK. Host only, no HIP call.
+ */
+dpp_status dpp_check_page_table(const dpp_plan* plan, const int32_t* kv_indices_host,
+                                int64_t num_kv_indices, int64_t num_pages);
 
 /*
  * Combine softmax partial states, the same device merge dpp_run uses for split rows.
+ *
+ * Defining passage: the fixed KV splits whose partial (o, lse) states are combined afterwards
+ * (model-serving-minefield issue #73, correction comment, "What the flag actually does",
+ * item 2); the combination is the log-sum-exp identity, taken in ascending split order.
  *
  *   o_partial   [num_rows, num_splits, num_heads, head_dim] fp32 device
  *   lse_partial [num_rows, num_splits, num_heads] fp32 device, natural log; -inf marks an

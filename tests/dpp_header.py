@@ -11,7 +11,7 @@ HEADER_WORDS = 16
 class ParsedPlan:
     requests: np.ndarray  # [B, 4]: q_start, qo_len, page_start, kv_len
     items: np.ndarray     # [N, 16]: request, row_start, split, tile_splits, kv_tile_begin, kv_tile_end,
-                          # slot_base, pad, then the request's q_start, qo_len, page_start, kv_len, pad x4
+                          # slot_base, pass, then the request's q_start, qo_len, page_start, kv_len, pad x4
     merges: np.ndarray    # [M, 4]: request, row_start, tile_splits, slot_base
     units: np.ndarray     # [U, 16]: persistent launches' unit records: the item's first 7 words,
                           # next, the request's 4 words, kv_head, block, pass, pad

@@ -56,9 +56,26 @@ def assert_close_to_oracle(o_gpu, lse_gpu, o_ref, lse_ref, rows=None, what=""):
     assert np.isfinite(lg).all(), f"{what}: non-finite lse"
     eo = np.abs(og - o_ref).max() if og.size else 0.0
     el = np.abs(lg - lse_ref).max() if lg.size else 0.0
-    say(f"{what}: max|o-oracle| = {eo:.3e}, max|lse-oracle| = {el:.3e}")
+    ulps, n_far = bf16_ulps(og, o_ref)
+    say(f"{what}: max|o-oracle| = {eo:.3e} ({ulps:.2f} bf16 ulps of the oracle rounded to bf16, "
+        f"{n_far} values beyond 2 ulps), max|lse-oracle| = {el:.3e}")
     assert eo <= O_TOL, f"{what}: max |o - oracle| = {eo}"
     assert el <= LSE_TOL, f"{what}: max |lse - oracle| = {el}"
+
+
+def bf16_ulps(o_gpu: np.ndarray, o_ref: np.ndarray):
+    """Error of bf16 outputs against the oracle rounded to bf16 (round to nearest even), in
+    units of that value's bf16 ulp, over values of magnitude >= 2^-6 (smaller ones are judged
+    by the absolute bound). Returns (max ulps, number of values beyond 2 ulps)."""
+    if o_gpu.size == 0:
+        return 0.0, 0
+    rne = torch.from_numpy(np.ascontiguousarray(o_ref, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+    big = np.abs(rne) >= 2.0 ** -6
+    if not big.any():
+        return 0.0, 0
+    ulp = np.exp2(np.floor(np.log2(np.abs(rne[big]))) - 7)
+    u = np.abs(o_gpu[big] - rne[big]) / ulp
+    return float(u.max()), int((u > 2).sum())
 
 
 def assert_bits_equal(a: torch.Tensor, b: torch.Tensor, what=""):

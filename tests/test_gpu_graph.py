@@ -2,7 +2,7 @@
 
 A captured launch reads the work list uploaded beforehand (reuse_upload), static q/o/lse and
 workspace buffers. Each replay, with eager work and synchronisations between replays, must
-give the eager run's bits. The extend batch is padded with zero-length requests to several
+match the oracle and give the eager run's bits. The extend batch is padded with zero-length requests to several
 capture sizes ("buckets"); in every bucket the real requests' rows must equal their full
 prefill's rows bit for bit -- nothing about the padded batch shape reaches a row.
 """
@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import workloads as wl
-from gpu_helpers import Device, assert_bits_equal, say
+from gpu_helpers import Device, assert_bits_equal, assert_close_to_oracle, oracle_rows, sample_rows, say
 
 pytestmark = pytest.mark.gpu
 
@@ -54,44 +54,60 @@ class Captured:
 
 
 @pytest.fixture(scope="module")
+def oracle():
+    import oracle as o
+    o.build(force=False)
+    return o
+
+
+@pytest.fixture(scope="module")
 def extend_work():
     return wl.extend_batch(layout="radix")
 
 
-def test_graph_replays_match_eager(extend_work):
+def test_graph_replays_match_eager(oracle, extend_work):
     dev = Device(extend_work)
-    cap = Captured(dev, extend_work.batches["cached"])
+    batch = extend_work.batches["cached"]
+    cap = Captured(dev, batch)
     other = extend_work.batches["full"]
+    ro, rl = oracle_rows(oracle, extend_work, batch)
     for i in range(4):
         say(f"replay {i}")
         o, l = cap.replay()
+        assert_close_to_oracle(o, l, ro, rl, what=f"extend replay {i} vs oracle")
         assert_bits_equal(o, cap.ref[0], f"replay {i} o")
         assert_bits_equal(l, cap.ref[1], f"replay {i} lse")
         dev.run(other)  # eager work between replays
 
 
-def test_graph_of_persistent_prefill():
+def test_graph_of_persistent_prefill(oracle):
     work = wl.cold_prefill(batch=4, length=1028)
     dev = Device(work)
-    cap = Captured(dev, work.batches["full"])
+    batch = work.batches["full"]
+    cap = Captured(dev, batch)
     assert cap.plan.info.num_prefill_items > 0
+    rows = sample_rows(batch, 40, seed=8)
+    ro, rl = oracle_rows(oracle, work, batch, rows)
     for i in range(3):
         say(f"prefill replay {i}")
         o, l = cap.replay()
+        assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"prefill replay {i} vs oracle")
         assert_bits_equal(o, cap.ref[0], f"prefill replay {i} o")
         assert_bits_equal(l, cap.ref[1], f"prefill replay {i} lse")
 
 
 @pytest.mark.parametrize("bucket", [16, 24, 32, 64])
-def test_graph_buckets_match_full_prefill(extend_work, bucket):
+def test_graph_buckets_match_full_prefill(oracle, extend_work, bucket):
     dev = Device(extend_work)
     cached, full = extend_work.batches["cached"], extend_work.batches["full"]
     o_f, l_f = dev.run(full)
     padded = _pad(cached, extend_work.prompts, extend_work.page_size, bucket)
     cap = Captured(dev, padded)
+    ro, rl = oracle_rows(oracle, extend_work, padded)
     for i in range(2):
         say(f"bucket {bucket} replay {i}")
         o, l = cap.replay()
+        assert_close_to_oracle(o, l, ro, rl, what=f"bucket {bucket} replay {i} vs oracle")
         assert_bits_equal(o, cap.ref[0], f"bucket {bucket} replay {i} o")
         for r in range(cached.batch_size):
             ia, ib = wl.matching_rows(padded, r, full, r)

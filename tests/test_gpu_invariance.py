@@ -108,3 +108,36 @@ def test_empty_and_degenerate_batches(oracle):
     empty = wl.sub_batch(b, work.prompts, 16, [0])
     o_e, l_e = dev.run(empty)
     assert o_e.shape[0] == 0 and l_e.shape[0] == 0
+
+
+PERMUTE_CASES = [
+    # (name, workload builder, batch, cap): a persistent mixed batch, narrow extends, fp8 with
+    # merges over several passes, the long-KV decode rows
+    ("mixed", lambda: wl.mixed_batch(), "mixed", None),
+    ("extend", lambda: wl.extend_batch(layout="distinct"), "cached", None),
+    ("fp8_split", lambda: wl.random_workload(10, hq=24, hkv=4, d=256, page_size=16, kv_dtype="fp8_e4m3",
+                                              specs=[(4100, 30), (8193, 1), (9000, 40), (300, 300)]),
+     "batch", 4 << 20),
+]
+
+
+@pytest.mark.parametrize("case", PERMUTE_CASES, ids=[c[0] for c in PERMUTE_CASES])
+def test_permuted_work_order_gives_the_same_bits(case):
+    """The test-only work permutation (items, merges, and so the workgroup, XCD and persistent
+    chain of every unit) changes no bit: the reduction order of a row is fixed by its own
+    position and the constants (sglang PR #46351 page, "Root cause")."""
+    name, build, which, cap = case
+    work = build()
+    dev = Device(work)
+    batch = work.batches[which]
+    o_ref, l_ref = dev.run(batch, cap=cap)
+    for seed in (1, 2, 3):
+        w = work
+        kw = dict(kv_dtype=w.kv_dtype, k_scale=w.k_scale, v_scale=w.v_scale, permute_seed=seed)
+        if cap is not None:
+            kw["workspace_cap"] = cap
+        p = dev.dpp.plan(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                         batch.qo_indptr, batch.kv_indptr, batch.kv_last_page_len, **kw)
+        o, l = dev.run(batch, plan=p)
+        assert_bits_equal(o, o_ref, f"{name} permutation {seed} o")
+        assert_bits_equal(l, l_ref, f"{name} permutation {seed} lse")

@@ -9,6 +9,7 @@ import pytest
 import torch
 
 import workloads as wl
+from dpp_header import parse
 from gpu_helpers import (Device, assert_bits_equal, assert_close_to_oracle, oracle_rows,
                          sample_rows, say)
 
@@ -143,15 +144,56 @@ def long_fp8_work():
     return wl.long_fp8()
 
 
-def test_long_fp8_parity(oracle, long_fp8_work):
+def pass_spread_rows(plan, batch, group: int, n_rows: int, seed: int) -> np.ndarray:
+    """About n_rows global q tokens spread over every pass of the plan and every split count:
+    the first and last token of each pass's tiles, the tokens on both sides of every
+    4096-token split boundary, and random tokens drawn pass by pass."""
+    parsed = parse(plan.header())
+    bm = plan.info.block_m
+    tiles = {}
+    for it in parsed.items:
+        r, rs, ps = int(it[0]), int(it[1]), int(it[7])
+        q_start, qo_len = int(parsed.requests[r][0]), int(parsed.requests[r][1])
+        rows = min(bm, qo_len * group - rs)
+        tiles[(r, rs)] = (ps, q_start + rs // group, q_start + (rs + rows - 1) // group)
+    passes = sorted({t[0] for t in tiles.values()})
+    rng = np.random.default_rng(seed)
+    pick = set()
+    per_pass = max(2, n_rows // len(passes))
+    for ps in passes:
+        spans = [(a, b) for (p_, a, b) in tiles.values() if p_ == ps]
+        lo, hi = min(a for a, _ in spans), max(b for _, b in spans)
+        pick |= {lo, hi}
+        toks = np.concatenate([np.arange(a, b + 1) for a, b in spans])
+        pick |= set(int(x) for x in rng.choice(toks, size=min(per_pass, toks.size), replace=False))
+    for r, req in enumerate(batch.requests):
+        a = int(batch.qo_indptr[r])
+        ctx = req.kv_len - req.qo_len
+        for boundary in range(4096, req.kv_len, 4096):
+            for pos in (boundary - 1, boundary):
+                if ctx <= pos < req.kv_len:
+                    pick.add(a + pos - ctx)
+    return np.array(sorted(pick), dtype=np.int64)
+
+
+@pytest.mark.parametrize("name", ["prefill_8192", "prefill_32768", "extend"])
+def test_long_fp8_parity(oracle, long_fp8_work, name):
+    """Hundreds of rows of each long fp8 batch against the oracle, spread over every pass of
+    the 256 MiB-capped plan and every split count (1-8 at 32,768 tokens)."""
     work = long_fp8_work
     dev = Device(work)
-    for name in ("prefill_8192", "extend"):
-        b = work.batches[name]
-        o, l = dev.run(b, cap=256 << 20)
-        rows = sample_rows(b, 6, seed=5)
-        ro, rl = oracle_rows(oracle, work, b, rows)
-        assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"long fp8 {name}")
+    b = work.batches[name]
+    p = dev.plan(b, cap=256 << 20)
+    o, l = dev.run(b, plan=p)
+    g = work.num_qo_heads // work.num_kv_heads
+    rows = pass_spread_rows(p, b, g, 280, seed=5)
+    splits = {(b.requests[0].kv_len - b.requests[0].qo_len + int(t)) // 4096 + 1 for t in rows}
+    say(f"long fp8 {name}: {p.info.num_passes} passes, {len(rows)} oracle rows, split counts {sorted(splits)}")
+    assert len(rows) >= 256
+    if name == "prefill_32768":
+        assert p.info.num_passes >= 10 and splits == set(range(1, 9))
+    ro, rl = oracle_rows(oracle, work, b, rows)
+    assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"long fp8 {name}")
 
 
 def test_long_fp8_extend_matches_32k_prefill(long_fp8_work):

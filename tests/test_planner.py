@@ -43,7 +43,7 @@ def test_library_exports_every_declared_symbol(dpp):
     assert declared, "no declarations parsed"
     assert declared <= exported, declared - exported
     assert declared == set(dpp.EXPORTS)
-    assert dpp.library().dpp_abi_version() == 2
+    assert dpp.library().dpp_abi_version() == 3
 
 
 def _plan(dpp, batch, hq=32, hkv=8, d=128, page=16, cap=0, **kw):
@@ -325,18 +325,24 @@ def test_run_rejects_bad_shapes_before_any_launch(dpp):
     p = _plan(dpp, b)
     fake = 1 << 20  # never dereferenced: every call below fails its host-side checks
     ws = p.workspace_bytes
-    st = lib.dpp_run(p._h, fake, 4, fake, fake, 64, fake, fake, fake, fake, ws, 0, None)
+    st = lib.dpp_run(p._h, fake, 4, fake, fake, 64, fake, 5, fake, fake, fake, ws, 0, None)
     assert st == dpp.DPP_ERR_SHAPE and b"q has 4 rows" in lib.dpp_last_error()
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake, ws - 1, 0, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, 5, fake, fake, fake, ws - 1, 0, None)
     assert st == dpp.DPP_ERR_WORKSPACE
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake + 16, ws, 0, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, 5, fake, fake, fake + 16, ws, 0, None)
     assert st == dpp.DPP_ERR_WORKSPACE  # misaligned workspace
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, None, ws, 0, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, 5, fake, fake, None, ws, 0, None)
     assert st == dpp.DPP_ERR_WORKSPACE
-    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, fake, fake, fake, ws, 4, None)
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, 5, fake, fake, fake, ws, 4, None)
     assert st == dpp.DPP_ERR_INVALID  # unknown flag
     st = lib.dpp_plan_upload(p._h, fake + 16, ws, None)
     assert st == dpp.DPP_ERR_WORKSPACE
+    # a page list shorter than kv_indptr[-1] (5 pages) would be read past its end on the device
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, 4, fake, fake, fake, ws, 0, None)
+    assert st == dpp.DPP_ERR_SHAPE and b"kv_indices holds 4" in lib.dpp_last_error()
+    # reusing an upload that never happened: the kernels would find no work list
+    st = lib.dpp_run(p._h, fake, 3, fake, fake, 64, fake, 5, fake, fake, fake, ws, 1, None)
+    assert st == dpp.DPP_ERR_INVALID and b"never uploaded" in lib.dpp_last_error()
     st = lib.dpp_merge_states(fake, fake, 1, 0, 1, 128, fake, fake, None)
     assert st == dpp.DPP_ERR_INVALID
     st = lib.dpp_merge_states(fake, fake, 1, 2, 1, 130, fake, fake, None)
@@ -405,7 +411,7 @@ def test_ragged_run_rejects_kv_beyond_the_tokens_passed(dpp):
     p = dpp.plan(32, 8, 128, 0, np.array([0, 3, 5], np.int32), np.array([0, 67, 107], np.int32))
     fake = 1 << 20
     ws = p.workspace_bytes
-    st = lib.dpp_run(p._h, fake, 5, fake, fake, 106, None, fake, fake, fake, ws, 0, None)
+    st = lib.dpp_run(p._h, fake, 5, fake, fake, 106, None, 0, fake, fake, fake, ws, 0, None)
     assert st == dpp.DPP_ERR_SHAPE and b"107 tokens" in lib.dpp_last_error()
 
 
@@ -438,7 +444,11 @@ def test_plan_create_ex_rejects_unknown_flags(dpp):
     cfg = dpp._Config(32, 8, 128, 16, 0, 0.0, 1.0, 1.0)
     h = ctypes.c_void_p()
     st = lib.dpp_plan_create_ex(ctypes.byref(cfg), 1, b.qo_indptr.ctypes.data, b.kv_indptr.ctypes.data,
-                                b.kv_last_page_len.ctypes.data, 0, 2, ctypes.byref(h))
+                                b.kv_last_page_len.ctypes.data, 0, 4, ctypes.byref(h))
+    assert st == dpp.DPP_ERR_INVALID and h.value is None
+    # a permutation seed without the permutation flag
+    st = lib.dpp_plan_create_ex(ctypes.byref(cfg), 1, b.qo_indptr.ctypes.data, b.kv_indptr.ctypes.data,
+                                b.kv_last_page_len.ctypes.data, 0, 5 << 16, ctypes.byref(h))
     assert st == dpp.DPP_ERR_INVALID and h.value is None
 
 
@@ -463,3 +473,123 @@ def test_head_dim_64_plans_like_128(dpp, specs):
     assert slots == p128.info.max_partial_slots
     if slots:
         assert p64.workspace_bytes - p64.info.header_bytes == _align(slots * 64 * 4) + _align(slots * 4)
+
+
+# ---- page-table contract (host check)
+
+def test_check_page_table(dpp):
+    """Every page id a request reads must lie in [0, num_pages); the host check names the first
+    one that does not, and a page list shorter than kv_indptr[-1] is a shape error."""
+    b = _specs_batch([(67, 3), (0, 0), (20, 20)])  # 5 + 0 + 2 pages
+    p = _plan(dpp, b)
+    ids = np.arange(7, dtype=np.int32) * 3
+    p.check_page_table(ids, num_pages=19)          # largest id 18
+    with pytest.raises(dpp.DppValueError, match="request 2, page 1: id 18"):
+        p.check_page_table(ids, num_pages=18)
+    bad = ids.copy()
+    bad[3] = -1
+    with pytest.raises(dpp.DppValueError, match="request 0, page 3: id -1"):
+        p.check_page_table(bad, num_pages=64)
+    with pytest.raises(dpp.DppValueError, match="kv_indices holds 6"):
+        p.check_page_table(ids[:6], num_pages=64)
+    # entries past kv_indptr[-1] are never read
+    p.check_page_table(np.concatenate([ids, [-5, 10**6]]).astype(np.int32), num_pages=19)
+    # ragged KV has no page table
+    pr = dpp.plan(32, 8, 128, 0, np.array([0, 3], np.int32), np.array([0, 67], np.int32))
+    pr.check_page_table(np.zeros(0, np.int32), num_pages=67)
+
+
+# ---- partial-slot invariant: the split-partial writes and the merge's reads stay inside the
+# pass's slot region, and only multi-split tiles own slots
+
+def _check_slot_invariant(parsed, hkv, g, bm, max_slots):
+    S_of_tile = {}
+    blocks = {}
+    for it in parsed.items:
+        r, rs, s, S, kb, ke, slot = (int(x) for x in it[:7])
+        q_start, qo_len, page_start, kv_len = (int(x) for x in parsed.requests[r])
+        rows = min(bm, qo_len * g - rs)
+        p_max = kv_len - qo_len + (rs + rows - 1) // g
+        assert S == p_max // 4096 + 1, "tile split count is its last row's"
+        S_of_tile.setdefault((r, rs), (S, slot))
+        assert S_of_tile[(r, rs)] == (S, slot), "every item of a tile carries the same slot block"
+        if S == 1:
+            assert slot == -1, f"single-split tile {(r, rs)} owns slot base {slot}"
+        else:
+            assert slot >= 0, f"multi-split tile {(r, rs)} has no slot block"
+            size = S * hkv * ((rows + 15) // 16 * 16)
+            assert slot + size <= max_slots, f"tile {(r, rs)} block [{slot}, {slot + size}) past {max_slots}"
+            blocks[(r, rs)] = (slot, slot + size)
+    merged = {(int(m[0]), int(m[1])): (int(m[2]), int(m[3])) for m in parsed.merges}
+    for key, (S, slot) in S_of_tile.items():
+        if S == 1:
+            assert key not in merged, f"single-split tile {key} has a merge item"
+        else:
+            assert merged[key] == (S, slot), f"merge item of {key} disagrees with its prefill items"
+    return blocks
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_partial_slots_stay_inside_each_pass(dpp, seed):
+    rng = np.random.default_rng(seed)
+    d = int(rng.choice([64, 128, 256]))
+    hkv = int(rng.choice([1, 2, 4, 8]))
+    g = int(rng.choice([1, 3, 4, 6]))
+    specs = []
+    for _ in range(int(rng.integers(1, 9))):
+        kv = int(rng.choice([rng.integers(0, 300), rng.integers(3000, 13000), rng.integers(4090, 4100)]))
+        ql = int(rng.choice([kv, min(kv, int(rng.integers(0, 40))), min(kv, 1)]))
+        specs.append((kv, ql))
+    b = _specs_batch(specs)
+    bm = dpp.tile_shape(d)[0]
+    # the largest single tile's partials decide the smallest cap that plans
+    need = 0
+    for kv, ql in specs:
+        for rs in range(0, ql * g, bm):
+            rows = min(bm, ql * g - rs)
+            S = (kv - ql + (rs + rows - 1) // g) // 4096 + 1
+            if S > 1:
+                need = max(need, S * hkv * ((rows + 15) // 16 * 16))
+    caps = [0, 256 << 20] + ([int(need * (d + 1) * 4 * f) + (4 << 20) for f in (1.0, 1.7, 3.1)] if need else [])
+    for cap in caps:
+        p = _plan(dpp, b, hq=hkv * g, hkv=hkv, d=d, cap=cap)
+        parsed = parse(p.header())
+        blocks = _check_slot_invariant(parsed, hkv, g, bm, p.info.max_partial_slots)
+        # unit records of persistent launches carry their tile's (tile_splits, slot_base)
+        for u in parsed.units:
+            r, rs, S, slot = int(u[0]), int(u[1]), int(u[3]), int(u[6])
+            assert slot == (-1 if S == 1 else blocks[(r, rs)][0])
+        if cap:
+            assert p.workspace_bytes <= cap
+        _check_disjoint_per_pass(p, parsed, blocks)
+
+
+def _check_disjoint_per_pass(p, parsed, blocks):
+    """Slot blocks of the tiles of one pass never overlap (each item records its pass)."""
+    by_pass = {}
+    for it in parsed.items:
+        key, ps = (int(it[0]), int(it[1])), int(it[7])
+        assert 0 <= ps < p.info.num_passes
+        if key in blocks:
+            by_pass.setdefault(ps, set()).add(blocks[key])
+    for ps, spans in by_pass.items():
+        spans = sorted(spans)
+        for (a0, a1), (b0, b1) in zip(spans, spans[1:]):
+            assert a1 <= b0, f"pass {ps}: slot blocks [{a0}, {a1}) and [{b0}, {b1}) overlap"
+
+
+@pytest.mark.parametrize("seed", [1, 2, 77])
+def test_permuted_plan_has_the_same_work(dpp, seed):
+    """The test-only permutation reorders items and merges inside each pass and nothing else."""
+    b = _specs_batch([(3700, 3700), (3701, 1), (3737, 37), (9000, 300), (1028, 1028), (5000, 4)])
+    base = _plan(dpp, b, cap=64 << 20)
+    perm = _plan(dpp, b, cap=64 << 20, permute_seed=seed)
+    pa, pb = parse(base.header()), parse(perm.header())
+    assert base.info == perm.info
+    key = lambda rows: sorted(tuple(int(x) for x in r) for r in rows)  # noqa: E731
+    assert key(pa.items) == key(pb.items)
+    assert key(pa.merges) == key(pb.merges)
+    assert [tuple(map(int, r)) for r in pa.items] != [tuple(map(int, r)) for r in pb.items]
+    # items stay in their pass
+    ps_a = [int(it[7]) for it in pa.items]
+    assert ps_a == sorted(ps_a) and [int(it[7]) for it in pb.items] == ps_a
