@@ -28,6 +28,7 @@ __all__ = ["plan", "Plan", "PlanInfo", "merge_states", "library", "LibraryNotBui
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libdpp.so")
 DEFAULT_WORKSPACE_CAP = 256 << 20
+STATIC_SCRATCH_BYTES = 32 << 20  # DPP_STATIC_SCRATCH_BYTES: plans for run_static stay under it
 SPLIT_TOKENS = 4096
 
 
@@ -87,7 +88,8 @@ class PlanInfo:
 
 _lib = None
 EXPORTS = ("dpp_plan_create", "dpp_plan_create_ex", "dpp_plan_workspace_bytes", "dpp_plan_get_info", "dpp_plan_header",
-           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_check_page_table", "dpp_merge_states",
+           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_run_static", "dpp_check_page_table",
+           "dpp_merge_states",
            "dpp_last_error", "dpp_status_string", "dpp_abi_version")
 
 
@@ -118,6 +120,8 @@ def library():
     lib.dpp_plan_destroy.argtypes = [vp]
     lib.dpp_run.restype = ctypes.c_int
     lib.dpp_run.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, sz, ctypes.c_uint32, vp]
+    lib.dpp_run_static.restype = ctypes.c_int
+    lib.dpp_run_static.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, ctypes.c_uint32, vp]
     lib.dpp_check_page_table.restype = ctypes.c_int
     lib.dpp_check_page_table.argtypes = [vp, vp, i64, i64]
     lib.dpp_merge_states.restype = ctypes.c_int

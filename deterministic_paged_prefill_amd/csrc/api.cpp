@@ -82,22 +82,22 @@ extern "C" dpp_status dpp_plan_upload(const dpp_plan* plan, void* workspace, siz
   return enqueue_upload(plan, workspace, (hipStream_t)stream);
 }
 
-extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows,
-                              const void* k_pool, const void* v_pool, int64_t num_pages,
-                              const int32_t* kv_indices, int64_t num_kv_indices, void* o, float* lse,
-                              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream_ptr) {
-  if (!plan) return fail(DPP_ERR_INVALID, "dpp_run: null plan");
+namespace dpp {
+
+dpp_status check_run_args(const dpp_plan* plan, const char* who, const void* q, int64_t q_rows,
+                          const void* k_pool, const void* v_pool, int64_t num_pages,
+                          const int32_t* kv_indices, int64_t num_kv_indices, const void* o,
+                          const float* lse, uint32_t flags) {
+  const std::string w(who);
+  if (!plan) return fail(DPP_ERR_INVALID, w + ": null plan");
   if (q_rows != plan->total_q_rows)
     return fail(DPP_ERR_SHAPE, "q has " + std::to_string(q_rows) + " rows but qo_indptr[-1] is " +
                                    std::to_string(plan->total_q_rows));
-  if (num_pages < 0) return fail(DPP_ERR_INVALID, "dpp_run: negative num_pages");
-  if (flags & ~DPP_RUN_REUSE_UPLOAD) return fail(DPP_ERR_INVALID, "dpp_run: unknown flags");
-  dpp_status st = check_workspace(plan, workspace, workspace_bytes);
-  if (st != DPP_OK) return st;
-  if (plan->total_q_rows > 0 && (!q || !o || !lse))
-    return fail(DPP_ERR_INVALID, "dpp_run: null q, o or lse");
+  if (num_pages < 0) return fail(DPP_ERR_INVALID, w + ": negative num_pages");
+  if (flags & ~DPP_RUN_REUSE_UPLOAD) return fail(DPP_ERR_INVALID, w + ": unknown flags");
+  if (plan->total_q_rows > 0 && (!q || !o || !lse)) return fail(DPP_ERR_INVALID, w + ": null q, o or lse");
   if (plan->num_items > 0 && (!k_pool || !v_pool || (!kv_indices && !plan->ragged)))
-    return fail(DPP_ERR_INVALID, "dpp_run: null k_pool, v_pool or kv_indices");
+    return fail(DPP_ERR_INVALID, w + ": null k_pool, v_pool or kv_indices");
   // ragged KV: num_pages counts the token rows of k_pool / v_pool, which every request's
   // [kv_indptr[r], kv_indptr[r+1]) must lie within (the kernels do not check it per key)
   if (plan->ragged && plan->total_kv_tokens > num_pages)
@@ -109,17 +109,15 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
                                    " page ids but kv_indptr[-1] is " + std::to_string(plan->total_kv_entries));
   if (!aligned(q, 16) || !aligned(o, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
       !aligned(lse, 4) || (!plan->ragged && !aligned(kv_indices, 4)))
-    return fail(DPP_ERR_INVALID, "dpp_run: q/o/k_pool/v_pool must be 16-byte aligned");
-  hipStream_t stream = (hipStream_t)stream_ptr;
-  if (plan->num_items == 0) return DPP_OK;
-  if (flags & DPP_RUN_REUSE_UPLOAD) {
-    st = check_reuse(plan, workspace);
-  } else {
-    st = enqueue_upload(plan, workspace, stream);
-  }
-  if (st != DPP_OK) return st;
-  hipError_t e;
+    return fail(DPP_ERR_INVALID, w + ": q/o/k_pool/v_pool must be 16-byte aligned");
+  return DPP_OK;
+}
 
+dpp_status launch_passes(const dpp_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                         int64_t num_pages, const int32_t* kv_indices, void* o, float* lse, void* workspace,
+                         void* stream_ptr) {
+  hipStream_t stream = (hipStream_t)stream_ptr;
+  hipError_t e;
   char* ws = (char*)workspace;
   PrefillArgs a{};
   a.q = q;
@@ -177,6 +175,28 @@ extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_row
     }
   }
   return DPP_OK;
+}
+
+}  // namespace dpp
+
+extern "C" dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows,
+                              const void* k_pool, const void* v_pool, int64_t num_pages,
+                              const int32_t* kv_indices, int64_t num_kv_indices, void* o, float* lse,
+                              void* workspace, size_t workspace_bytes, uint32_t flags, void* stream_ptr) {
+  dpp_status st = check_run_args(plan, "dpp_run", q, q_rows, k_pool, v_pool, num_pages, kv_indices, num_kv_indices,
+                                 o, lse, flags);
+  if (st != DPP_OK) return st;
+  st = check_workspace(plan, workspace, workspace_bytes);
+  if (st != DPP_OK) return st;
+  hipStream_t stream = (hipStream_t)stream_ptr;
+  if (plan->num_items == 0) return DPP_OK;
+  if (flags & DPP_RUN_REUSE_UPLOAD) {
+    st = check_reuse(plan, workspace);
+  } else {
+    st = enqueue_upload(plan, workspace, stream);
+  }
+  if (st != DPP_OK) return st;
+  return launch_passes(plan, q, k_pool, v_pool, num_pages, kv_indices, o, lse, workspace, stream_ptr);
 }
 
 extern "C" dpp_status dpp_check_page_table(const dpp_plan* plan, const int32_t* kv_indices_host,

@@ -65,4 +65,16 @@ dpp_status fail(dpp_status st, const std::string& msg);
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Host checks of a run's arguments (everything but the workspace), shared by the entry points.
+dpp_status check_run_args(const dpp_plan* plan, const char* who, const void* q, int64_t q_rows,
+                          const void* k_pool, const void* v_pool, int64_t num_pages,
+                          const int32_t* kv_indices, int64_t num_kv_indices, const void* o,
+                          const float* lse, uint32_t flags);
+
+// Enqueue the prefill and merge launches of every pass over a workspace that holds the plan's
+// work list (stream-ordered after its upload).
+dpp_status launch_passes(const dpp_plan* plan, const void* q, const void* k_pool, const void* v_pool,
+                         int64_t num_pages, const int32_t* kv_indices, void* o, float* lse, void* workspace,
+                         void* stream);
+
 }  // namespace dpp

@@ -226,6 +226,33 @@ dpp_status dpp_run(const dpp_plan* plan, const void* q, int64_t q_rows, const vo
                    int64_t num_kv_indices, void* o, float* lse, void* workspace,
                    size_t workspace_bytes, uint32_t flags, void* stream);
 
+/* Size of the scratch array dpp_run_static uses in place of a workspace (32 MiB per device). */
+#define DPP_STATIC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * dpp_run without a workspace, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc. It calls no
+ * hipMalloc, hipFree or other allocating routine. The work list and the split partials live
+ * in a file-scope device array of DPP_STATIC_SCRATCH_BYTES, one per device, held by the
+ * library until the process ends; the caller still passes q, the pools, the page list and the
+ * outputs, with dpp_run's layouts, checks and bits.
+ *
+ *   flags   0 (upload the plan's work list into the device's scratch, from the plan's pinned
+ *           copy if an earlier dpp_run made one, else from its host memory), or
+ *           DPP_RUN_REUSE_UPLOAD when the last dpp_run_static on this device uploaded this
+ *           same plan (otherwise DPP_ERR_INVALID)
+ *
+ * A plan whose workspace exceeds DPP_STATIC_SCRATCH_BYTES is DPP_ERR_WORKSPACE before any HIP
+ * call: plan with workspace_cap_bytes <= DPP_STATIC_SCRATCH_BYTES, which bounds every plan by
+ * running more passes. Every call on one device shares that device's scratch and leaves its
+ * contents behind: calls that overlap on one GPU (other streams, other threads) race, and
+ * must be ordered by the caller. Other errors as dpp_run.
+ */
+dpp_status dpp_run_static(const dpp_plan* plan, const void* q, int64_t q_rows, const void* k_pool,
+                          const void* v_pool, int64_t num_pages, const int32_t* kv_indices,
+                          int64_t num_kv_indices, void* o, float* lse, uint32_t flags,
+                          void* stream);
+
 /*
  * Host check of a page table against a plan: kv_indices_host holds at least kv_indptr[B]
  * entries and every page id that a request of the plan reads lies in [0, num_pages).

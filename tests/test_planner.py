@@ -593,3 +593,21 @@ def test_permuted_plan_has_the_same_work(dpp, seed):
     # items stay in their pass
     ps_a = [int(it[7]) for it in pa.items]
     assert ps_a == sorted(ps_a) and [int(it[7]) for it in pb.items] == ps_a
+
+
+def test_run_static_refuses_plans_above_its_scratch(dpp):
+    """dpp_run_static checks the plan against its fixed scratch before any HIP call."""
+    lib = dpp.library()
+    b = _specs_batch([(8192, 8192)])
+    big = _plan(dpp, b, hq=24, hkv=4, d=256, cap=0)
+    assert big.workspace_bytes > dpp.STATIC_SCRATCH_BYTES
+    fake = 1 << 20
+    st = lib.dpp_run_static(big._h, fake, 8192, fake, fake, 600, fake, 512, fake, fake, 0, None)
+    assert st == dpp.DPP_ERR_WORKSPACE and b"static scratch" in lib.dpp_last_error()
+    # the same batch planned under the scratch's size fits, in more passes
+    small = _plan(dpp, b, hq=24, hkv=4, d=256, cap=dpp.STATIC_SCRATCH_BYTES)
+    assert small.workspace_bytes <= dpp.STATIC_SCRATCH_BYTES and small.info.num_passes > 1
+    st = lib.dpp_run_static(small._h, fake, 8191, fake, fake, 600, fake, 512, fake, fake, 0, None)
+    assert st == dpp.DPP_ERR_SHAPE  # dpp_run's argument checks come first
+    st = lib.dpp_run_static(small._h, fake, 8192, fake, fake, 600, fake, 512, fake, fake, 2, None)
+    assert st == dpp.DPP_ERR_INVALID
