@@ -20,7 +20,9 @@ others    the remaining configurations, each timed and its cached-vs-full bits c
 decode    8 one-token decodes over 8k-128k keys each (same shapes, 2-32 KV splits a row, the
           split partials merged): logical KV bytes / step time (1.4 GB of KV, far past the
           Infinity Cache).
-roofline  the extend kernel against HBM (8 TB/s); prefill's own against bf16 MFMA peak.
+roofline  the extend kernel against HBM (8 TB/s), and against a measured ceiling: the
+          read-only streaming reference (dpp_stream_kv) gathering the same pages with no
+          compute; prefill's own against bf16 MFMA peak.
 cpu_baseline  the fp64 CPU oracle on the same extend batch, repeated for ~10 s.
 """
 from __future__ import annotations
@@ -129,6 +131,35 @@ class Runner:
         wall_ms = (time.perf_counter() - t0) * 1e3
         return start.elapsed_time(end) / steps, wall_ms / steps
 
+    def stream_timed(self, split: int, depth: int, steps: int, warmup: int) -> float:
+        """ms per launch of the read-only streaming reference (dpp_stream_kv) over the same pages,
+        rotated like the attention steps."""
+        import torch
+        args = [(self.plan._h, self.k.data_ptr(), self.v.data_ptr(), self.k.shape[0], kvi.data_ptr(),
+                 kvi.numel(), self.ws.data_ptr(), self.ws.numel(), split, depth, self.dpp.RUN_REUSE_UPLOAD,
+                 self.stream.cuda_stream) for kvi in self.kvi]
+        for i in range(warmup):
+            self.dpp._check(self.lib.dpp_stream_kv(*args[i % self.replicas]))
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        start.record(self.stream)
+        for i in range(steps):
+            self.lib.dpp_stream_kv(*args[(warmup + i) % self.replicas])
+        end.record(self.stream)
+        torch.cuda.synchronize()
+        return start.elapsed_time(end) / steps
+
+    def stream_ceiling(self, steps: int, warmup: int) -> dict:
+        """Best of the streaming reference's grids (1 or 2 workgroups per unit, 4 or 8 loads in
+        flight per wave): the measured ceiling of this gather on this GPU."""
+        best = None
+        for split in (1, 2):
+            for depth in (4, 8):
+                ms = self.stream_timed(split, depth, steps, warmup)
+                if best is None or ms < best[0]:
+                    best = (ms, split, depth)
+        return dict(ms=best[0], split=best[1], depth=best[2])
+
     def graph_timed(self, steps_per_graph: int, replays: int):
         """The same steps captured in one HIP graph (torch.cuda.graph over dpp_run, work list
         uploaded beforehand) and replayed: ms per step."""
@@ -207,7 +238,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-others", action="store_true")
-    ap.add_argument("--only", choices=["extend", "prefill", "decode", "copy"], default=None,
+    ap.add_argument("--only", choices=["extend", "prefill", "decode", "copy", "stream"], default=None,
                     help="run one leg only and print its timing (for profiler runs)")
     args = ap.parse_args()
 
@@ -241,6 +272,12 @@ def main() -> int:
     result = {}
 
     # ---------------------------------------------------------------- extend (value)
+    if args.only == "stream":  # profiler run: the streaming reference over the extend pages
+        work = wl.extend_batch(layout="distinct")
+        run = Runner(work, work.batches["cached"], replicas=args.replicas)
+        ms = run.stream_timed(2, 4, args.steps, args.warmup)
+        log(f"stream reference: {ms * 1e3:.2f} us/launch")
+        return 0
     if args.only in (None, "extend"):
         log("building extend workload (distinct pages)")
         work = wl.extend_batch(layout="distinct")
@@ -264,13 +301,14 @@ def main() -> int:
         log(f"cached-vs-full max|diff| = {max_diff}")
         ms, wall = run.timed(args.steps, args.warmup)
         ms_graph = run.graph_timed(40, 10)
+        ceiling = run.stream_ceiling(args.steps, args.warmup)
         nbytes = kv_bytes(cached, hkv, d, 2)
         io_bytes = (2 * cached.num_q_tokens * hq * d * 2 + cached.num_q_tokens * hq * 4
                     + cached.kv_indices.size * 4)
         alg = nbytes + io_bytes
         achieved = alg / (ms * 1e-3) / 1e9
         result["extend"] = dict(ms=ms, wall_ms=wall, graph_ms=ms_graph, kv_bytes=nbytes, alg_bytes=alg, gbps=nbytes / (ms * 1e-3) / 1e9,
-                                achieved=achieved, plan_us=run.plan_us, upload_us=run.upload_us,
+                                achieved=achieved, plan_us=run.plan_us, upload_us=run.upload_us, ceiling=ceiling,
                                 max_diff=max_diff, work=work, batch=cached,
                                 items=run.plan.info.num_prefill_items)
         # radix layout (prefix pages physically shared): logical bytes over a cache-served read
@@ -319,13 +357,14 @@ def main() -> int:
         bd = work_d.batches["decode"]
         dr = Runner(work_d, bd, replicas=1)
         ms_d, _ = dr.timed(max(10, args.steps // 4), max(5, args.warmup // 4))
+        ceil_d = dr.stream_ceiling(max(10, args.steps // 4), 3) if args.only is None else None
         if args.only == "decode":
             log(f"decode: {ms_d * 1e3:.2f} us/step")
             return 0
         nb = kv_bytes(bd, hkv, d, 2)
         result["decode"] = dict(ms=ms_d, kv_bytes=nb, gbps=nb / (ms_d * 1e-3) / 1e9,
                                 items=dr.plan.info.num_prefill_items,
-                                merges=dr.plan.info.num_merge_items,
+                                merges=dr.plan.info.num_merge_items, ceiling=ceil_d,
                                 workspace=dr.plan.info.workspace_bytes)
         del dr
 
@@ -411,7 +450,15 @@ def main() -> int:
         "cached_vs_full_max_abs_diff": ext["max_diff"],
         "roofline": {"bound": "hbm", "achieved": round(ext["achieved"], 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(ext["achieved"] / HBM_PEAK_GBPS, 4),
-                     "traffic": None if traffic is None else round(traffic)},
+                     "traffic": None if traffic is None else round(traffic),
+                     "measured_ceiling": {
+                         "what": "read-only streaming reference (dpp_stream_kv): the same KV pages, "
+                                 "rotated pools and work list, gathered into LDS and dropped, no compute",
+                         "us_per_launch": round(ext["ceiling"]["ms"] * 1e3, 2),
+                         "kv_gbps": round(ext["kv_bytes"] / (ext["ceiling"]["ms"] * 1e-3) / 1e9, 1),
+                         "workgroups_per_unit": ext["ceiling"]["split"],
+                         "loads_in_flight_per_wave": ext["ceiling"]["depth"],
+                         "frac": round(ext["ceiling"]["ms"] / ext["ms"], 4)}},
         "extend_detail": {"us_per_step": round(ext["ms"] * 1e3, 2),
                           "host_wall_us_per_step": round(ext["wall_ms"] * 1e3, 2),
                           "graph_replay_us_per_step": round(ext["graph_ms"] * 1e3, 2),
@@ -448,7 +495,11 @@ def main() -> int:
                           "merge_items": dd["merges"], "workspace_bytes": dd["workspace"],
                           "roofline": {"bound": "hbm", "achieved": round(dd["gbps"], 2),
                                        "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                                       "frac": round(dd["gbps"] / HBM_PEAK_GBPS, 4)}}
+                                       "frac": round(dd["gbps"] / HBM_PEAK_GBPS, 4),
+                                       "measured_ceiling": None if dd["ceiling"] is None else {
+                                           "us_per_launch": round(dd["ceiling"]["ms"] * 1e3, 2),
+                                           "kv_gbps": round(dd["kv_bytes"] / (dd["ceiling"]["ms"] * 1e-3) / 1e9, 1),
+                                           "frac": round(dd["ceiling"]["ms"] / dd["ms"], 4)}}}
     if others:
         line["other_configs"] = others
     if not args.no_cpu_baseline:

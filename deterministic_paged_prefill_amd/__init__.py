@@ -88,7 +88,8 @@ class PlanInfo:
 
 _lib = None
 EXPORTS = ("dpp_plan_create", "dpp_plan_create_ex", "dpp_plan_workspace_bytes", "dpp_plan_get_info", "dpp_plan_header",
-           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_run_static", "dpp_check_page_table",
+           "dpp_plan_upload", "dpp_plan_destroy", "dpp_run", "dpp_run_static", "dpp_stream_kv",
+           "dpp_check_page_table",
            "dpp_merge_states",
            "dpp_last_error", "dpp_status_string", "dpp_abi_version")
 
@@ -122,6 +123,8 @@ def library():
     lib.dpp_run.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, vp, sz, ctypes.c_uint32, vp]
     lib.dpp_run_static.restype = ctypes.c_int
     lib.dpp_run_static.argtypes = [vp, vp, i64, vp, vp, i64, vp, i64, vp, vp, ctypes.c_uint32, vp]
+    lib.dpp_stream_kv.restype = ctypes.c_int
+    lib.dpp_stream_kv.argtypes = [vp, vp, vp, i64, vp, i64, vp, sz, i32, i32, ctypes.c_uint32, vp]
     lib.dpp_check_page_table.restype = ctypes.c_int
     lib.dpp_check_page_table.argtypes = [vp, vp, i64, i64]
     lib.dpp_merge_states.restype = ctypes.c_int

@@ -254,6 +254,20 @@ dpp_status dpp_run_static(const dpp_plan* plan, const void* q, int64_t q_rows, c
                           void* stream);
 
 /*
+ * Read-only streaming reference of a plan's KV gather (a measurement tool, not part of the
+ * attention): every K and V byte the plan's prefill units read, each once, is moved into LDS
+ * by LDS-DMA and dropped, by `split` workgroups per unit (item, kv head) with `depth` (4, 8, 16
+ * or 32) 1 KiB loads in flight per wave. Its time is the ceiling the memory-bound launches of
+ * the same plan (short extends, long-KV decodes) are measured against. Arguments as dpp_run;
+ * paged plans only; flags 0 or DPP_RUN_REUSE_UPLOAD (the workspace already holds this plan's
+ * work list). Writes only the workspace head.
+ */
+dpp_status dpp_stream_kv(const dpp_plan* plan, const void* k_pool, const void* v_pool,
+                         int64_t num_pages, const int32_t* kv_indices, int64_t num_kv_indices,
+                         void* workspace, size_t workspace_bytes, int32_t split, int32_t depth,
+                         uint32_t flags, void* stream);
+
+/*
  * Host check of a page table against a plan: kv_indices_host holds at least kv_indptr[B]
  * entries and every page id that a request of the plan reads lies in [0, num_pages).
  * DPP_ERR_SHAPE names the first offending (request, page); DPP_ERR_INVALID on null or
