@@ -425,6 +425,18 @@ def main() -> int:
                      "prefills of 8,192 and 32,768 tokens, a 1,024-token extend behind 31,744 cached tokens",
             **legs)
         del outs
+        log("head_dim 512")
+        w6 = wl.random_workload(512, hq=16, hkv=4, d=512, page_size=16, kv_dtype="bf16", specs=[(2048, 4)] * 4)
+        b6e, b6f = w6.batches["batch"], w6.batches["full"]
+        ms6f, o6f, l6f, _ = timed_leg(w6, b6f, 10, 5)
+        ms6e, o6e, l6e, _ = timed_leg(w6, b6e, 50, 10)
+        fl6 = causal_flops(b6f, 16, 512)
+        others["head_dim_512"] = {
+            "workload": "16 q / 4 kv heads, head_dim 512, bf16, page 16: cold prefill of 4 x 2,048 tokens, "
+                        "and 4-token extends of the same prompts behind 2,044 cached tokens",
+            "prefill_us": round(ms6f * 1e3, 2), "prefill_causal_flops": fl6,
+            "prefill_tflops": round(fl6 / (ms6f * 1e-3) / 1e12, 2), "extend_us": round(ms6e * 1e3, 2),
+            "cached_vs_full_max_abs_diff": bits_equal(b6e, o6e, l6e, b6f, o6f, l6f, [(i, i) for i in range(4)])}
 
     ext = result["extend"]
     traffic = traffic_from_profile(ext["alg_bytes"])

@@ -34,7 +34,7 @@ SPLIT_TOKENS = 4096
 
 def tile_shape(head_dim: int) -> tuple:
     """(packed query rows, keys) of one tile: constants of head_dim (see dpp_internal.h)."""
-    return (256, 64) if head_dim <= 128 else (128, 32)
+    return {64: (256, 64), 128: (256, 64), 256: (128, 32), 512: (64, 32)}[head_dim]
 
 DPP_OK, DPP_ERR_INVALID, DPP_ERR_SHAPE, DPP_ERR_UNSUPPORTED, DPP_ERR_WORKSPACE, DPP_ERR_HIP = range(6)
 RUN_REUSE_UPLOAD = 1

@@ -20,10 +20,12 @@ namespace dpp {
 
 // Tile geometry: constants of head_dim, never of the batch.
 // A packed query row is (token, q head within the kv head's group); row R of a request covers
-// token R / group and q head kv_head * group + R % group. Every wave owns 32 packed rows as
-// two 16-row MFMA column blocks; a workgroup is 8 waves (two per SIMD, 256-row tiles) at
-// head_dim <= 128 and 4 waves (one per SIMD, 128-row tiles) at head_dim 256.
-DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim <= 128 ? 32 : 32; }
+// token R / group and q head kv_head * group + R % group. A wave owns 32 packed rows as two
+// 16-row MFMA column blocks at head_dim <= 256 and one 16-row block at head_dim 512 (where a
+// row's fp32 output alone takes 128 registers of a wave's lanes); a workgroup is 8 waves (two
+// per SIMD, 256-row tiles) at head_dim <= 128, 4 waves (one per SIMD) at 256 (128-row tiles)
+// and 512 (64-row tiles).
+DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim <= 256 ? 32 : 16; }
 DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 128 ? 8 : 4; }
 DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) {
   return rows_per_wave_for(head_dim) * waves_for(head_dim);
@@ -35,9 +37,13 @@ constexpr int kNarrowRows = 16;
 // Keys per KV tile. Tiles start at absolute key positions 0, BN, 2BN, ...
 DPP_HOST_DEVICE constexpr int block_n_for(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 constexpr int kMaxBlockM = 256;
-// LDS of a workgroup: a ring of four K and four V tiles (bf16), then page-id tables (4 bytes
-// an entry; two in a persistent launch, one per unit in flight), within the 160 KiB of a CU.
-DPP_HOST_DEVICE constexpr int ring_bytes_for(int head_dim) { return 2 * 4 * block_n_for(head_dim) * head_dim * 2; }
+// LDS of a workgroup: a ring of K and V tiles (bf16) -- four of each, two at head_dim 512
+// whose 32-key tiles are 32 KiB -- then page-id tables (4 bytes an entry; two in a persistent
+// launch, one per unit in flight), within the 160 KiB of a CU.
+DPP_HOST_DEVICE constexpr int ring_buffers_for(int head_dim) { return head_dim <= 256 ? 4 : 2; }
+DPP_HOST_DEVICE constexpr int ring_bytes_for(int head_dim) {
+  return 2 * ring_buffers_for(head_dim) * block_n_for(head_dim) * head_dim * 2;
+}
 constexpr int kLdsLimit = 160 * 1024;
 // Output staging of the two-group schedule: 2 KiB for each wave of a group.
 constexpr int kOutStageBytes = 4 * 2048;

@@ -152,6 +152,8 @@ hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipS
     hipLaunchKernelGGL(merge_kernel<128>, grid, dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 256)
     hipLaunchKernelGGL(merge_kernel<256>, grid, dim3(kMergeThreads), 0, stream, a);
+  else if (head_dim == 512)
+    hipLaunchKernelGGL(merge_kernel<512>, grid, dim3(kMergeThreads), 0, stream, a);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

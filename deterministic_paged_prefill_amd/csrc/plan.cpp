@@ -160,9 +160,9 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
     return fail(DPP_ERR_UNSUPPORTED,
                 "num_qo_heads must be a positive multiple of num_kv_heads (got " +
                     std::to_string(c.num_qo_heads) + "/" + std::to_string(c.num_kv_heads) + ")");
-  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256)
+  if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256 && c.head_dim != 512)
     return fail(DPP_ERR_UNSUPPORTED, "head_dim " + std::to_string(c.head_dim) +
-                                         " not built (64, 128 and 256 are)");
+                                         " not built (64, 128, 256 and 512 are)");
   if (c.page_size < 0 || c.page_size > 1024)
     return fail(DPP_ERR_UNSUPPORTED, "page_size must be in [1, 1024], or 0 for ragged KV");
   if (c.kv_dtype != DPP_KV_BF16 && c.kv_dtype != DPP_KV_FP8_E4M3)

@@ -78,7 +78,7 @@ struct Geo {
   static constexpr int CH = D / 8;                 // 16-byte bf16 chunks per K/V row
   static constexpr int ROW_BYTES = D * 2;
   static constexpr int TILE_BYTES = BN * ROW_BYTES;  // one KV tile of K or V in bf16
-  static constexpr int NBUF = 4;                   // LDS buffers per tensor
+  static constexpr int NBUF = ring_buffers_for(D);  // LDS buffers per tensor (4, or 2 at D = 512)
   static constexpr int KB = BN / 16;               // 16-key blocks (QK M blocks)
   static constexpr int DC = D / 32;                // 32-wide head_dim chunks (QK k-steps)
   static constexpr int DB = D / 16;                // 16-wide head_dim blocks (PV M blocks)
@@ -454,7 +454,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const bool issuer = !kSpec || (wave & 2) != 0;
   constexpr int NL = C::TILE_BYTES / (IW * 1024);         // their loads per tensor per tile
   constexpr int NCHT = FP8 ? C::NCH : NL;                 // chunks per thread per tensor per tile
-  constexpr int KA = kPP ? 3 : C::NBUF;                   // load group t brings K(t + KA), V(t + 2)
+  constexpr int KA = kPP ? 3 : C::NBUF;                   // load group t brings K(t + KA), V(t + VA)
+  constexpr int VA = C::NBUF - 2;
   const unsigned char* zero16 = reinterpret_cast<const unsigned char*>(pre->zero_chunk);
   int krow[NCHT];        // key row inside the tile
   int kcol[NCHT];        // byte offset of the K chunk inside the kv head's part of a token row
@@ -533,11 +534,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 
   // LDS: K buffers 0..NBUF-1, then V buffers 0..NBUF-1; tile t uses buffers t % NBUF.
   // Load group t brings K(t + NBUF) and V(t + NBUF - 2). It is issued in iteration t and
-  // complete before the barrier that ends iteration t + 2; iteration t reads K(t + 1) and
-  // V(t - 1). K(t + NBUF) replaces K(t), last read in iteration t - 1 (K(0): in the
+  // complete before the barrier that ends iteration t + NBUF - 2; iteration t reads K(t + 1)
+  // and V(t - 1). K(t + NBUF) replaces K(t), last read in iteration t - 1 (K(0): in the
   // prologue, which ends with a barrier for it), and V(t + NBUF - 2) replaces V(t - 2), last
-  // read in iteration t - 1.
-  static_assert(C::NBUF == 4, "the schedule below assumes four buffers");
+  // read in iteration t - 1. With two buffers (head_dim 512) a group is complete within its own
+  // iteration; the narrow two-wave and two-group schedules are built for four.
+  static_assert(C::NBUF == 4 || (C::NBUF == 2 && !kSpec && !kPP), "ring depth of the schedules");
   const uint32_t lds0 = (uint32_t)(uintptr_t)smem;  // LDS byte address of the dynamic block
   // LDS byte offset of ring buffer t of K or V
   auto kbuf_off = [&](int t) { return (t & (C::NBUF - 1)) * C::TILE_BYTES; };
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   };
   auto issue_group = [&](int t) {  // bf16: DMA of load group t
     dma_tile(false, t + KA);
-    dma_tile(true, t + 2);
+    dma_tile(true, t + VA);
   };
   // Scalar pages. Load i of this wave in tile t covers key rows [key0, key0 + KPI) of one
   // page; its page id is read from the LDS table one iteration ahead (a uniform read that
@@ -610,7 +612,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 #pragma unroll
     for (int i = 0; i < NCHT; ++i) {
       ids[0][i] = pg_lds[page_slot(g + KA, i)];
-      ids[1][i] = pg_lds[page_slot(g + 2, i)];
+      ids[1][i] = pg_lds[page_slot(g + VA, i)];
     }
   };
   // Descriptors of the next group's loads, prepared ahead so that firing a load is an M0
@@ -626,7 +628,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     for (int j = 0; j < kLoads; ++j) {
       const bool v = j >= NCHT;
       const int i = v ? j - NCHT : j;
-      const int t = v ? grp + 2 : grp + KA;
+      const int t = v ? grp + VA : grp + KA;
       const int id = __builtin_amdgcn_readfirstlane(ids[v ? 1 : 0][i]);
       const bool good = id >= 0 && id < a.num_pages;  // else the load reads zeros
       const uint64_t base = reinterpret_cast<uint64_t>(v ? vbase : kbase);
@@ -1004,7 +1006,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
           for (int t = -C::NBUF; t < 0; ++t) issue_group(t);
         }
       }
-      wait_vmcnt<2 * kGroupLoads>();  // groups -4 and -3 landed: K(0), K(1), V(-1)
+      // groups -NBUF and -NBUF + 1 landed: K(0), K(1), and V(-1) (zeros)
+      wait_vmcnt<(C::NBUF - 2) * kGroupLoads>();
     }
     __syncthreads();
     if (has_rows) qk(s, 0);
@@ -1015,6 +1018,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       if constexpr (FP8) {
         fp8_store(t + C::NBUF - 1, t + C::NBUF - 3);  // group t-1
         fp8_load(t + C::NBUF, t + C::NBUF - 2);       // group t
+        // with two buffers the tiles just stored, K(t + 1) and V(t - 1), are this iteration's
+        if constexpr (C::NBUF == 2) __syncthreads();
       } else if constexpr (MODE == kPagesScalar) {
         if (issuer) issue_group_scalar(t);
       } else {
@@ -1027,10 +1032,15 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         softmax(s, pb, alpha, std::true_type{});
         qk(s, t + 1);
       }
-      if constexpr (!FP8) wait_vmcnt<2 * kGroupLoads>();  // group t-2 landed
+      if constexpr (!FP8) wait_vmcnt<(C::NBUF - 2) * kGroupLoads>();  // group t + 2 - NBUF landed
       __syncthreads();
     };
     for (int t = 0; t < n_tiles; ++t) iteration(t);
+    if constexpr (FP8 && C::NBUF == 2) {
+      // with two buffers the last V tile arrives in group n_tiles - 1, which no iteration stores
+      fp8_store(n_tiles + 1, n_tiles - 1);
+      __syncthreads();
+    }
     if (has_rows) pv_acc(pb, n_tiles - 1, no_hook);
   } else {
     // Two groups: waves 0-3 lead, waves 4-7 (which share the SIMDs with them pairwise) run
@@ -1251,6 +1261,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool
   if (head_dim == 64) return launch_d<64>(a, fp8, narrow, stream);
   if (head_dim == 128) return launch_d<128>(a, fp8, narrow, stream);
   if (head_dim == 256) return launch_d<256>(a, fp8, narrow, stream);
+  if (head_dim == 512) return launch_d<512>(a, fp8, narrow, stream);
   return hipErrorInvalidValue;
 }
 

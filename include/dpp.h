@@ -75,7 +75,7 @@ typedef enum { DPP_KV_BF16 = 0, DPP_KV_FP8_E4M3 = 1 } dpp_kv_dtype;
 typedef struct {
   int32_t num_qo_heads;  /* Hq, a multiple of num_kv_heads */
   int32_t num_kv_heads;  /* Hkv */
-  int32_t head_dim;      /* 64, 128 or 256 */
+  int32_t head_dim;      /* 64, 128, 256 or 512 */
   int32_t page_size;     /* tokens per page, 1..1024; 0 = ragged (contiguous) KV */
   int32_t kv_dtype;      /* dpp_kv_dtype */
   float sm_scale;        /* softmax scale; 0 selects 1/sqrt(head_dim) */

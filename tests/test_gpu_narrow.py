@@ -4,7 +4,7 @@ A pass runs on the narrow instantiation only when every tile in it is narrow, so
 hold nothing but short extends and one-token rows: 1-4 tokens at a GQA group of 4 (16 rows),
 1-2 at a group of 6 (12 rows), behind prefixes of 300-9,000 tokens, among them rows on both
 sides of the 4,096-token split boundary. They cover every narrow instantiation that ships:
-fp8 E4M3 at head_dim 128 and 256, bf16 at 64, 128 and 256, with per-lane power-of-two page
+fp8 E4M3 at head_dim 128, 256 and 512, bf16 at 64, 128, 256 and 512, with per-lane power-of-two page
 addressing (page 16) and general addressing (pages 12 and 1,024), and at head_dim 128 both
 the head_dim-split launch (few units) and the one-workgroup-per-unit launch (many units).
 
@@ -28,6 +28,8 @@ SHAPES = {  # name: (hq, hkv, d, kv_dtype)
     "bf16_d64": (16, 4, 64, "bf16"),
     "bf16_d128": (32, 8, 128, "bf16"),
     "bf16_d256": (24, 4, 256, "bf16"),
+    "bf16_d512": (16, 4, 512, "bf16"),
+    "fp8_d512": (16, 4, 512, "fp8_e4m3"),
 }
 
 

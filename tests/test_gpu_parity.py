@@ -66,6 +66,13 @@ RANDOM_CASES = [
     # the largest page size (one page holds a whole short prompt) and a 32-wide GQA group
     (16, 32, 8, 128, 1024, "bf16", [(3000, 3000), (3001, 5), (1025, 1), (1024, 2)]),
     (17, 64, 2, 128, 16, "bf16", [(200, 200), (201, 3), (33, 1)]),
+    # head_dim 512 (64-row x 32-key tiles, a two-deep LDS ring): wide and narrow tiles, rows
+    # across the 4096 split, per-lane power-of-two pages (16, 1) and general addressing (12, 64)
+    (18, 16, 4, 512, 16, "bf16", [(300, 300), (301, 3), (70, 1), (129, 16), (64, 64), (4100, 12)]),
+    (19, 16, 4, 512, 16, "fp8_e4m3", [(200, 200), (201, 2), (4100, 8), (33, 33)]),
+    (20, 8, 2, 512, 1, "bf16", [(150, 150), (151, 4)]),
+    (21, 8, 2, 512, 12, "fp8_e4m3", [(130, 130), (131, 1), (4097, 2)]),
+    (22, 8, 8, 512, 64, "bf16", [(180, 180), (181, 35), (7, 7)]),
 ]
 
 

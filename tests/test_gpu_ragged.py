@@ -65,6 +65,10 @@ CASES = {
                                              specs=[(160, 160), (161, 5), (70, 1)]), "batch"),
     "bf16_d64": lambda: (wl.random_workload(11, hq=16, hkv=4, d=64, page_size=16, kv_dtype="bf16",
                                             specs=[(300, 300), (301, 3), (70, 1), (4100, 12)]), "batch"),
+    "bf16_d512": lambda: (wl.random_workload(18, hq=16, hkv=4, d=512, page_size=16, kv_dtype="bf16",
+                                             specs=[(300, 300), (301, 3), (70, 1), (4100, 12)]), "batch"),
+    "fp8_d512": lambda: (wl.random_workload(19, hq=16, hkv=4, d=512, page_size=16, kv_dtype="fp8_e4m3",
+                                            specs=[(200, 200), (201, 2), (4100, 8)]), "batch"),
 }
 
 

@@ -47,7 +47,7 @@ def wl_dense(q, k, v, pos, scale):
 
 
 @pytest.mark.parametrize("hq,hkv,d,page", [(4, 4, 8, 3), (8, 2, 8, 1), (12, 2, 16, 16),
-                                           (6, 1, 128, 5), (32, 8, 128, 16)])
+                                           (6, 1, 128, 5), (32, 8, 128, 16), (8, 2, 512, 4)])
 def test_oracle_matches_numpy_brute_force(oracle_lib, hq, hkv, d, page):
     specs = [(1, 1), (9, 4), (23, 23), (40, 17), (37, 1), (16, 0)]
     work = wl.random_workload(7 + hq + page, hq=hq, hkv=hkv, d=d, page_size=page,

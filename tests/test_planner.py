@@ -298,7 +298,7 @@ def test_malformed_batches_are_rejected(dpp, mutate, status):
 
 @pytest.mark.parametrize("args,status", [
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=96), "DPP_ERR_UNSUPPORTED"),
-    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=512), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=32, num_kv_heads=8, head_dim=1024), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=30, num_kv_heads=8, head_dim=128), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=-1), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1025), "DPP_ERR_UNSUPPORTED"),
@@ -473,6 +473,29 @@ def test_head_dim_64_plans_like_128(dpp, specs):
     assert slots == p128.info.max_partial_slots
     if slots:
         assert p64.workspace_bytes - p64.info.header_bytes == _align(slots * 64 * 4) + _align(slots * 4)
+
+
+@pytest.mark.parametrize("specs", [[(1028, 1028)], [(1025, 1), (4100, 12), (8200, 2), (300, 0)],
+                                   [(9000, 9000), (67, 3)]])
+def test_head_dim_512_tiles(dpp, specs):
+    """head_dim 512: 64 packed rows x 32 keys a tile (4 waves of one 16-row block), every needed
+    (row, split) covered, no persistent chains, partial slots of (512 + 1) floats."""
+    g = 4
+    b = _specs_batch(specs, g=g)
+    p = _plan(dpp, b, hq=32, hkv=8, d=512)
+    assert (p.info.block_m, p.info.block_n) == (64, 32) == dpp.tile_shape(512)
+    a = parse(p.header())
+    assert len(a.units) == 0
+    cov = _coverage(a, g, 64)
+    for r, (kv, qlen) in enumerate(specs):
+        for R in range(qlen * g):
+            pos = kv - qlen + R // g
+            for s in range(pos // 4096 + 1):
+                kb, ke = cov[(r, R, s)]
+                assert kb == s * 128 and ke * 32 > min(pos, (s + 1) * 4096 - 1) and ke <= (s + 1) * 128
+    slots = p.info.max_partial_slots
+    if slots:
+        assert p.workspace_bytes - p.info.header_bytes == _align(slots * 512 * 4) + _align(slots * 4)
 
 
 # ---- page-table contract (host check)
