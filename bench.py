@@ -227,6 +227,65 @@ def cpu_baseline(work, batch, budget_s: float):
                       f"{reps} repetitions in {el:.1f} s"}
 
 
+def row_flops(batch, hq: int, d: int, rows) -> float:
+    """Causal FLOPs of the given global query rows: 4 d Hq (p + 1) each."""
+    import numpy as np
+    pos = np.empty(batch.num_q_tokens, dtype=np.int64)
+    for r, req in enumerate(batch.requests):
+        a = int(batch.qo_indptr[r])
+        pos[a:a + req.qo_len] = np.arange(req.kv_len - req.qo_len, req.kv_len)
+    return 4.0 * d * hq * float((pos[np.asarray(rows, dtype=np.int64)] + 1).sum())
+
+
+def cpu_baseline_configs(budget_s: float) -> dict:
+    """The oracle on every other configuration: seeded row samples of each (every stride-th
+    query row, stride chosen for about budget_s seconds in all), timed and extrapolated to the
+    whole batch by causal FLOPs (the oracle's cost is linear in them)."""
+    import numpy as np
+
+    import oracle
+    import workloads as wl
+    oracle.build(force=False)
+    cases = [
+        ("single_extend_67 (full prefill)", wl.single_extend, "full"),
+        ("cold_prefill_16x1028", wl.cold_prefill, "full"),
+        ("mixed_3700_plus_7_tails", wl.mixed_batch, "mixed"),
+        ("long_fp8 prefill_8192", wl.long_fp8, "prefill_8192"),
+        ("long_fp8 prefill_32768", wl.long_fp8, "prefill_32768"),
+        ("long_fp8 extend_1024_behind_31744", wl.long_fp8, "extend"),
+        ("decode_8x1_over_8k-128k", lambda: wl.decode_batch(full_prompts=0), "decode"),
+    ]
+    out = {}
+    per_case = budget_s / len(cases)
+    works = {}
+    for name, build, which in cases:
+        if build not in works:
+            works[build] = build()
+        work = works[build]
+        b = work.batches[which]
+        n = b.num_q_tokens
+        total = causal_flops(b, work.num_qo_heads, work.head_dim)
+        # probe one row to size the sample, then time the sample
+        probe = np.array([n - 1])
+        t0 = time.perf_counter()
+        oracle.paged_prefill(**work.oracle_kwargs(b), rows=probe)
+        t_probe = max(time.perf_counter() - t0, 1e-4)
+        f_probe = row_flops(b, work.num_qo_heads, work.head_dim, probe)
+        want = max(1, int(per_case / t_probe * f_probe / (total / n)))
+        stride = max(1, n // want)
+        rows = np.arange(stride // 2, n, stride, dtype=np.int64)
+        t0 = time.perf_counter()
+        oracle.paged_prefill(**work.oracle_kwargs(b), rows=rows)
+        el = time.perf_counter() - t0
+        f_rows = row_flops(b, work.num_qo_heads, work.head_dim, rows)
+        full_s = el * total / f_rows
+        out[name] = {"sample_rows": int(rows.size), "of_rows": n, "sample_s": round(el, 3),
+                     "extrapolated_full_s": round(full_s, 3),
+                     "tflops": round(total / full_s / 1e12, 5)}
+    del works
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -517,6 +576,8 @@ def main() -> int:
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
         line["cpu_baseline"] = cpu_baseline(ext["work"], ext["batch"], args.cpu_budget_s)
+        log("timing the CPU oracle on the other configurations (row samples)")
+        line["cpu_baseline"]["other_configs"] = cpu_baseline_configs(args.cpu_budget_s)
     print(json.dumps(line), flush=True)
     return 0
 

@@ -18,7 +18,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libdpp.so")
-SOURCES = ["plan.cpp", "api.cpp", "prefill.hip", "merge.hip", "static_run.hip", "stream_ref.hip"]
+SOURCES = ["plan.cpp", "checks.cpp", "api.cpp", "prefill.hip", "merge.hip", "static_run.hip", "stream_ref.hip"]
 ARCH = "gfx950"
 
 
