@@ -131,6 +131,29 @@ class Runner:
         wall_ms = (time.perf_counter() - t0) * 1e3
         return start.elapsed_time(end) / steps, wall_ms / steps
 
+    def replan_us(self, n: int = 20) -> tuple:
+        """Host cost of a new batch of the same shape, as a serving loop pays it every batch:
+        (plan us, upload us) medians over n rounds, each plan destroyed before the next (its
+        pinned staging block goes back to the library's pool), into a workspace of its own."""
+        import numpy as np
+        import torch
+        w, b = self.work, self.batch
+        ws = self.plan.new_workspace("cuda")
+        plan_t, up_t = [], []
+        for _ in range(n):
+            t0 = time.perf_counter()
+            p = self.dpp.plan(w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                              b.qo_indptr, b.kv_indptr, b.kv_last_page_len, kv_dtype=w.kv_dtype,
+                              k_scale=w.k_scale, v_scale=w.v_scale)
+            t1 = time.perf_counter()
+            p.upload(ws, self.stream)
+            torch.cuda.synchronize()
+            t2 = time.perf_counter()
+            p.close()
+            plan_t.append(t1 - t0)
+            up_t.append(t2 - t1)
+        return float(np.median(plan_t) * 1e6), float(np.median(up_t) * 1e6)
+
     def stream_timed(self, split: int, depth: int, steps: int, warmup: int) -> float:
         """ms per launch of the read-only streaming reference (dpp_stream_kv) over the same pages,
         rotated like the attention steps."""
@@ -361,6 +384,7 @@ def main() -> int:
         ms, wall = run.timed(args.steps, args.warmup)
         ms_graph = run.graph_timed(40, 10)
         ceiling = run.stream_ceiling(args.steps, args.warmup)
+        replan = run.replan_us()
         nbytes = kv_bytes(cached, hkv, d, 2)
         io_bytes = (2 * cached.num_q_tokens * hq * d * 2 + cached.num_q_tokens * hq * 4
                     + cached.kv_indices.size * 4)
@@ -368,6 +392,7 @@ def main() -> int:
         achieved = alg / (ms * 1e-3) / 1e9
         result["extend"] = dict(ms=ms, wall_ms=wall, graph_ms=ms_graph, kv_bytes=nbytes, alg_bytes=alg, gbps=nbytes / (ms * 1e-3) / 1e9,
                                 achieved=achieved, plan_us=run.plan_us, upload_us=run.upload_us, ceiling=ceiling,
+                                replan=replan,
                                 max_diff=max_diff, work=work, batch=cached,
                                 items=run.plan.info.num_prefill_items)
         # radix layout (prefix pages physically shared): logical bytes over a cache-served read
@@ -536,6 +561,8 @@ def main() -> int:
                           "algorithmic_bytes_per_launch": ext["alg_bytes"],
                           "work_items": ext["items"], "plan_us": round(ext["plan_us"], 1),
                           "upload_us": round(ext["upload_us"], 1),
+                          "next_batch_plan_us": round(ext["replan"][0], 1),
+                          "next_batch_upload_us": round(ext["replan"][1], 1),
                           "radix_layout_logical_gbps": round(ext["radix_logical_gbps"], 1),
                           "radix_layout_us_per_step": round(ext["radix_ms"] * 1e3, 2)},
         "adaptive_tile_control": {

@@ -1,12 +1,15 @@
 // Launch glue of libdpp: argument checks, work-list upload, kernel launches.
 //
 // Nothing here allocates or frees device memory or synchronises a stream. The only HIP
-// allocation is the plan's pinned host copy of its work list (made on first use, so that
-// planning itself stays HIP-free).
+// allocation is the pinned host staging copy of a plan's work list (made on its first upload,
+// so that planning itself stays HIP-free), taken from a library-wide pool of pinned blocks
+// that destroyed plans return to: a serving loop that plans every batch reuses them instead
+// of allocating pinned memory per batch.
 #include <hip/hip_runtime.h>
 
 #include <cstddef>
 #include <cstring>
+#include <map>
 #include <string>
 
 #include "kernels.h"
@@ -22,12 +25,56 @@ dpp_status hip_fail(hipError_t e, const char* what) {
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
+// Pool of pinned staging blocks, sizes rounded up to powers of two (64 KiB and up). A block
+// goes back to the pool when its plan is destroyed -- after the stream work that read it, which
+// the plan's lifetime contract guarantees -- and the pool keeps at most kPinnedPoolBytes.
+constexpr size_t kPinnedMinBytes = 64 << 10;
+constexpr size_t kPinnedPoolBytes = 64 << 20;
+std::mutex g_pool_mu;
+std::multimap<size_t, void*> g_pool;
+size_t g_pool_bytes = 0;
+
+size_t pinned_class(size_t bytes) {
+  size_t c = kPinnedMinBytes;
+  while (c < bytes) c <<= 1;
+  return c;
+}
+
+hipError_t pinned_get(size_t bytes, void** out, size_t* cap) {
+  const size_t c = pinned_class(bytes);
+  {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    auto it = g_pool.find(c);
+    if (it != g_pool.end()) {
+      *out = it->second;
+      *cap = c;
+      g_pool_bytes -= c;
+      g_pool.erase(it);
+      return hipSuccess;
+    }
+  }
+  *cap = c;
+  return hipHostMalloc(out, c, hipHostMallocDefault);
+}
+
+void pinned_put(void* p, size_t cap) {
+  {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    if (g_pool_bytes + cap <= kPinnedPoolBytes) {
+      g_pool.emplace(cap, p);
+      g_pool_bytes += cap;
+      return;
+    }
+  }
+  (void)hipHostFree(p);
+}
+
 }  // namespace
 
 
 extern "C" void dpp_plan_destroy(dpp_plan* plan) {
   if (!plan) return;
-  if (plan->pinned) (void)hipHostFree(plan->pinned);
+  if (plan->pinned) pinned_put(plan->pinned, plan->pinned_cap);
   delete plan;
 }
 
@@ -48,10 +95,12 @@ dpp_status enqueue_upload(const dpp_plan* plan, void* workspace, hipStream_t str
     std::lock_guard<std::mutex> lock(plan->pinned_mu);
     if (!plan->pinned) {
       void* p = nullptr;
-      hipError_t e = hipHostMalloc(&p, hbytes, hipHostMallocDefault);
+      size_t cap = 0;
+      hipError_t e = pinned_get(hbytes, &p, &cap);
       if (e != hipSuccess) return hip_fail(e, "hipHostMalloc(work list)");
       std::memcpy(p, plan->header.data(), hbytes);
       plan->pinned = p;
+      plan->pinned_cap = cap;
     }
   }
   hipError_t e = hipMemcpyAsync(workspace, plan->pinned, hbytes, hipMemcpyHostToDevice, stream);

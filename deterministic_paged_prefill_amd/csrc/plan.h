@@ -52,6 +52,7 @@ struct dpp_plan {
   // Pinned host copy of `header`, created on first dpp_run (plan creation stays HIP-free).
   mutable std::mutex pinned_mu;
   mutable void* pinned = nullptr;
+  mutable size_t pinned_cap = 0;  // bytes of the pinned block (a pool size class)
   // Workspace of the last enqueued upload of this plan's work list (guarded by pinned_mu):
   // a run that reuses an upload must name the same workspace.
   mutable const void* uploaded_ws = nullptr;

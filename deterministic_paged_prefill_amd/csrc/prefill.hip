@@ -1076,8 +1076,11 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     constexpr int kEvery = (C::KC * C::DB) / kLoads;
     static_assert(kEvery >= 1, "one load per PV step at most");
     for (;;) {
-      // Q (unless loaded ahead) and load group -3 (K(0)); the trailing waves' rows of the
-      // previous unit. The full wait below covers Q either way.
+      // Q (unless loaded ahead) and load group -3 (K(0)). The full wait below covers Q either
+      // way. The trailing waves write the previous unit's rows after the barrier, ahead of the
+      // next loads: a store counts on the same counter as the loads, so the wait here would
+      // hold every wave until the stores are acknowledged, while after the barrier their
+      // acknowledgement is due only at the trailing waves' wait for group -2.
       if (!q_ready) load_q();
       q_ready = false;
       if constexpr (MODE == kPagesScalar) {
@@ -1086,12 +1089,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       } else {
         issue(-3);
       }
+      wait_vmcnt<0>();
+      __syncthreads();
       if (!leading && has_prev) {
         write_out(rcur);  // still the previous unit's record
         reset_state();
       }
-      wait_vmcnt<0>();
-      __syncthreads();
       if (rotate) {
         rcur = rnext;
         rnext = rfetch;
