@@ -21,12 +21,12 @@ namespace dpp {
 // Tile geometry: constants of head_dim, never of the batch.
 // A packed query row is (token, q head within the kv head's group); row R of a request covers
 // token R / group and q head kv_head * group + R % group. A wave owns 32 packed rows as two
-// 16-row MFMA column blocks at head_dim <= 256 and one 16-row block at head_dim 512 (where a
-// row's fp32 output alone takes 128 registers of a wave's lanes); a workgroup is 8 waves (two
-// per SIMD, 256-row tiles) at head_dim <= 128, 4 waves (one per SIMD) at 256 (128-row tiles)
-// and 512 (64-row tiles).
-DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim <= 256 ? 32 : 16; }
-DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 128 ? 8 : 4; }
+// 16-row MFMA column blocks at head_dim <= 128 and one 16-row block at 256 and 512 (where a
+// row's fp32 output takes 64 and 128 registers of a wave's lanes); a workgroup is 8 waves (two
+// per SIMD: 256-row tiles at head_dim <= 128, 128-row tiles at 256) or 4 waves (one per SIMD,
+// 64-row tiles) at 512.
+DPP_HOST_DEVICE constexpr int rows_per_wave_for(int head_dim) { return head_dim <= 128 ? 32 : 16; }
+DPP_HOST_DEVICE constexpr int waves_for(int head_dim) { return head_dim <= 256 ? 8 : 4; }
 DPP_HOST_DEVICE constexpr int block_m_for(int head_dim) {
   return rows_per_wave_for(head_dim) * waves_for(head_dim);
 }
@@ -67,7 +67,7 @@ DPP_HOST_DEVICE inline int xcd_chunked(int b, int n) {
   return x * q + (x < r ? x : r) + b / kXcds;
 }
 
-// Persistent launches. A wide bf16 launch at head_dim <= 128 (eight waves) runs as this many
+// Persistent launches. A wide bf16 launch at head_dim <= 256 (eight waves) runs as this many
 // workgroups -- one per compute unit of an MI355X; the LDS ring leaves room for one workgroup
 // per CU -- each working through a chain of units (item, kv head) fixed by the planner. The
 // chain a unit lands in decides when it runs, never its arithmetic.

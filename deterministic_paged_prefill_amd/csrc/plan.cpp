@@ -15,7 +15,7 @@
 //  * order: inside a pass, requests with the longest item first, a request's items kept
 //    together and longest first (load balance, and L2 reuse of the request's KV); a pass of
 //    tiles with at most kNarrowRows rows each runs on the narrow kernel;
-//  * persistent chains: a wide bf16 pass at head_dim <= 128 runs as kPersistentBlocks
+//  * persistent chains: a wide bf16 pass at head_dim <= 256 runs as kPersistentBlocks
 //    workgroups, each over a chain of units (item, kv head). The units that the plain launch
 //    order would send to XCD x (a contiguous run, see xcd_chunked) are dealt longest first
 //    to the least loaded of the workgroups on XCD x (b % kXcds == x), each chain then

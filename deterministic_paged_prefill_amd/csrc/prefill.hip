@@ -1,12 +1,13 @@
 // Causal GQA prefill attention over a paged KV cache, gfx950 (CDNA4), wave64.
 //
 // A unit = one (q tile, KV split, kv head); a workgroup runs one unit, or in a persistent
-// launch a chain of units. Each wave owns 32 packed rows as two 16-row MFMA column blocks;
-// 8 waves (two per SIMD, 256-row tiles) at head_dim 64 and 128, 4 waves (one per SIMD,
-// 128-row tiles) at head_dim 256. Per KV tile of BN keys (64 at head_dim 128, 32 at head_dim 256;
-// tiles start at absolute multiples of BN):
+// launch a chain of units. 8 waves, two per SIMD: each wave owns 32 packed rows as two
+// 16-row MFMA column blocks at head_dim 64 and 128 (256-row tiles), one 16-row block at 256
+// (128-row tiles); at head_dim 512, 4 waves of one block (64-row tiles). Per KV tile of BN
+// keys (64 at head_dim <= 128, 32 above; tiles start at absolute multiples of BN):
 //   gather   16-byte chunks of K and V rows come through the page table straight into a ring
-//            of four K and four V LDS buffers by LDS-DMA, several tiles ahead (natural
+//            of four K and four V LDS buffers (two of each at head_dim 512) by LDS-DMA,
+//            several tiles ahead (natural
 //            [key][d] layout, 16-byte chunks XOR-swizzled by key). Keys past kv_len or on an
 //            out-of-range page read zeros; fp8 E4M3 chunks go through registers and are
 //            decoded to bf16 on the way.
@@ -236,13 +237,15 @@ constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2;
 // all of K; each loads only its half of V's columns and writes its half of the output. Every
 // output element still accumulates the same MFMA sequence, so the bits are those of one
 // workgroup; the unit's bytes per workgroup drop to 3/4 and twice the workgroups stream them.
-template <int D, bool FP8, int NB, int MODE, bool VH, int BNX>
+// NARROW: the instantiation for passes of tiles with at most kNarrowRows rows (NB = 1).
+template <int D, bool FP8, int NB, bool NARROW, int MODE, bool VH, int BNX>
 __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillArgs a) {
   using C = Geo<D, NB, BNX>;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   // Narrow bf16 kernel with eight waves: wave 0 computes scores and softmax, wave 4 (on the
   // same SIMD) the output, and waves 2, 3, 6, 7 issue the DMA loads.
-  constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
+  static_assert(!NARROW || NB == 1, "a narrow tile is one 16-row block");
+  constexpr bool kSpec = !FP8 && NARROW && waves_for(D) == 8;
   static_assert(!VH || (kSpec && MODE != kPagesScalar), "head_dim halves: narrow bf16 kernel, vector addresses");
   // V ring: rows of head_dim (or of half of it, VH) per tile
   constexpr int VROW = VH ? C::ROW_BYTES / 2 : C::ROW_BYTES;
@@ -251,7 +254,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   constexpr int VDB = VH ? C::DB / 2 : C::DB;  // PV head_dim blocks of this workgroup
   // Two-group schedule (see below): bf16 wide tiles with two waves per SIMD. Its launches may
   // be persistent (a chain of units per workgroup).
-  constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
+  constexpr bool kPP = !FP8 && !NARROW && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
   unsigned char* xb = smem + RING;  // exchange buffer (kSpec)
   // page-id tables after the ring: raw ids from kv_indices, 4 bytes an entry; a persistent
   // launch alternates between two (the next unit's ids load during the current unit)
@@ -1174,30 +1177,30 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   }
 }
 
-template <int D, bool FP8, int NB, int MODE, bool VH = false, int BNX = block_n_for(D)>
+template <int D, bool FP8, int NB, bool NARROW, int MODE, bool VH = false, int BNX = block_n_for(D)>
 hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
   using C = Geo<D, NB, BNX>;
   constexpr int kRing = C::NBUF * (C::TILE_BYTES + (VH ? C::TILE_BYTES / 2 : C::TILE_BYTES));
   // page-id tables (4 bytes an entry): a unit's pages plus one tile's worth of slack for the
   // last tile's lookups past kv_len (their chunks read the zero chunk); two in a persistent
   // launch
-  constexpr bool kSpec = !FP8 && NB == 1 && waves_for(D) == 8;
+  constexpr bool kSpec = !FP8 && NARROW && waves_for(D) == 8;
   const size_t pt_bytes = (size_t)page_table_bytes(a.page_slots, D);
-  constexpr bool kPP = !FP8 && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
+  constexpr bool kPP = !FP8 && !NARROW && C::WAVES == 8 && NB * 16 == rows_per_wave_for(D);
   const size_t lds = (size_t)kRing + (kSpec ? C::XBYTES : 0) + (a.chain_offset >= 0 ? 2 : 1) * pt_bytes +
                      (kPP ? (size_t)kOutStageBytes : 0);
   if (lds > (size_t)kLdsLimit) return hipErrorInvalidValue;
   static int lds_opt_in = 0;  // largest dynamic LDS size requested so far
   if ((int)lds > lds_opt_in) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, MODE, VH, BNX>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<D, FP8, NB, NARROW, MODE, VH, BNX>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     lds_opt_in = (int)lds;
   }
   if (VH && a.chain_offset >= 0) return hipErrorInvalidValue;
   dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains : (VH ? 2 : 1) * a.num_items * a.num_kv_heads));
-  if (a.chain_offset >= 0 && !chained_launch(D, FP8, NB == 1)) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, MODE, VH, BNX>), grid, dim3(C::THREADS), lds, stream, a);
+  if (a.chain_offset >= 0 && !chained_launch(D, FP8, NARROW)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, NARROW, MODE, VH, BNX>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();
 }
 
@@ -1215,40 +1218,43 @@ int compute_units() {
   return v;
 }
 
-template <int D, int NB, int BNX = block_n_for(D)>
+template <int D, int NB, bool NARROW, int BNX = block_n_for(D)>
 hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   const int P = a.page_size;
   const bool pow2 = (P & (P - 1)) == 0;
   if constexpr (BNX == block_n_for(D)) {
-    if (fp8) {
-      return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, kPagesPow2>(a, stream)
-                                         : launch_one<D, true, NB, kPagesGeneral>(a, stream);
+    if (fp8) {  // one fp8 schedule: NARROW changes nothing in it
+      return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, false, kPagesPow2>(a, stream)
+                                         : launch_one<D, true, NB, false, kPagesGeneral>(a, stream);
     }
   } else if (fp8) {
     return hipErrorInvalidValue;  // the comparison tile is built for bf16 only
   }
   // The narrow kernel's issuing waves compute nothing else: per-lane (vector) addresses
-  // suit them. The wide kernel's waves are busy with the softmax: scalar descriptors.
-  if constexpr (NB > 1) {
-    if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, kPagesScalar>(a, stream);
-  } else if constexpr (waves_for(D) == 8 && D >= 128) {
+  // suit them. The wide eight-wave kernel's waves are busy with the softmax: scalar
+  // descriptors.
+  if constexpr (!NARROW && waves_for(D) == 8) {
+    if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, NARROW, kPagesScalar>(a, stream);
+  } else if constexpr (NARROW && waves_for(D) == 8 && D >= 128) {
     // A narrow launch of at most one unit per two compute units splits head_dim in PV over
     // two workgroups per unit (same bits). A CU streams a unit's gather at a rate of its own,
     // so two CUs that each load all of K and half of V (3/4 of the unit's bytes) finish sooner
     // than one that loads all of it, while the K they share comes from HBM once.
     if (2 * a.num_items * a.num_kv_heads <= compute_units()) {
-      return pow2 && P <= BNX ? launch_one<D, false, NB, kPagesPow2, true, BNX>(a, stream)
-                              : launch_one<D, false, NB, kPagesGeneral, true, BNX>(a, stream);
+      return pow2 && P <= BNX ? launch_one<D, false, NB, NARROW, kPagesPow2, true, BNX>(a, stream)
+                              : launch_one<D, false, NB, NARROW, kPagesGeneral, true, BNX>(a, stream);
     }
   }
-  return pow2 && P <= BNX ? launch_one<D, false, NB, kPagesPow2, false, BNX>(a, stream)
-                          : launch_one<D, false, NB, kPagesGeneral, false, BNX>(a, stream);
+  return pow2 && P <= BNX ? launch_one<D, false, NB, NARROW, kPagesPow2, false, BNX>(a, stream)
+                          : launch_one<D, false, NB, NARROW, kPagesGeneral, false, BNX>(a, stream);
 }
 
 template <int D>
 hipError_t launch_d(const PrefillArgs& a, bool fp8, bool narrow, hipStream_t stream) {
   constexpr int kWide = rows_per_wave_for(D) / 16;
-  return narrow ? launch_nb<D, 1>(a, fp8, stream) : launch_nb<D, kWide>(a, fp8, stream);
+  // four-wave head dims have no narrow specialisation: one instantiation serves both
+  constexpr bool kNarrowKernel = waves_for(D) == 8;
+  return narrow ? launch_nb<D, 1, kNarrowKernel>(a, fp8, stream) : launch_nb<D, kWide, false>(a, fp8, stream);
 }
 
 }  // namespace
@@ -1258,7 +1264,7 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool
   const bool fp8 = kv_dtype == 1;
   if (block_n != block_n_for(head_dim)) {
     // adaptive-tile comparison plans only: narrow bf16 tiles with 32 keys at head_dim 128
-    if (head_dim == 128 && block_n == 32 && narrow && !fp8) return launch_nb<128, 1, 32>(a, false, stream);
+    if (head_dim == 128 && block_n == 32 && narrow && !fp8) return launch_nb<128, 1, true, 32>(a, false, stream);
     return hipErrorInvalidValue;
   }
   if (head_dim == 64) return launch_d<64>(a, fp8, narrow, stream);

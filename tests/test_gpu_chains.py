@@ -1,14 +1,16 @@
 """GPU tests of persistent launches (chains of units per workgroup).
 
-A wide bf16 launch at head_dim 128 runs as 256 workgroups, each over a chain of units
-(q tile, KV split, kv head) that the planner fixes; between units a workgroup swaps page-id
-tables, reloads Q and its first K/V tiles while writing the previous unit's rows. These cases
-have more than 256 units (chains longer than one), a request crossing the 4096-token split
-(partials inside chains), ragged last tiles and every page-addressing mode of the wide kernel:
-scalar descriptors (page size a power of two >= 4), per-lane power-of-two (2) and general
-(12); page size 1 does not fit two page tables and runs one unit per workgroup. Each case is
-checked against the oracle on sampled rows, and requests run alone (chains of their own
-units only) must give the same bits as inside the batch.
+A wide bf16 launch of the eight-wave kernel (head_dim 128: 256-row tiles of two 16-row blocks
+a wave; head_dim 256: 128-row tiles of one block a wave) runs as 256 workgroups, each over a
+chain of units (q tile, KV split, kv head) that the planner fixes; between units a workgroup
+swaps page-id tables, reloads Q and its first K/V tiles while writing the previous unit's
+rows. These cases have more than 256 units (chains longer than one), a request crossing the
+4096-token split (partials inside chains), ragged last tiles and every page-addressing mode of
+the wide kernel: scalar descriptors (page size a power of two holding at least one wave-wide
+load's key rows: 4 at head_dim 128, 2 at 256), per-lane power-of-two (2 at head_dim 128) and
+general (12); page size 1 does not fit two page tables and runs one unit per workgroup. Each
+case is checked against the oracle on sampled rows, and requests run alone (chains of their
+own units only) must give the same bits as inside the batch.
 """
 import numpy as np
 import pytest
@@ -19,6 +21,7 @@ from gpu_helpers import Device, assert_bits_equal, assert_close_to_oracle, oracl
 pytestmark = pytest.mark.gpu
 
 SPECS = [(1500, 1500), (1200, 700), (4300, 300), (900, 900), (77, 77), (260, 33)]
+SHAPES = {"d128": (32, 8, 128), "d256": (24, 4, 256)}  # hq, hkv, head_dim
 
 
 @pytest.fixture(scope="module")
@@ -28,15 +31,17 @@ def oracle():
     return o
 
 
+@pytest.mark.parametrize("shape", list(SHAPES))
 @pytest.mark.parametrize("page", [16, 4, 2, 12, 1])
-def test_chains_against_oracle_and_alone(oracle, page):
-    work = wl.random_workload(700 + page, hq=32, hkv=8, d=128, page_size=page, kv_dtype="bf16",
+def test_chains_against_oracle_and_alone(oracle, page, shape):
+    hq, hkv, d = SHAPES[shape]
+    work = wl.random_workload(700 + page + d, hq=hq, hkv=hkv, d=d, page_size=page, kv_dtype="bf16",
                               specs=SPECS)
     dev = Device(work)
     batch = work.batches["batch"]
     plan = dev.plan(batch)
     units = len(__import__("dpp_header").parse(plan.header()).units)
-    say(f"page {page}: {plan.info.num_prefill_items} items, {units} unit records")
+    say(f"{shape} page {page}: {plan.info.num_prefill_items} items, {units} unit records")
     if page > 1:
         assert units > 256, "chains longer than one unit"
     else:
@@ -44,23 +49,25 @@ def test_chains_against_oracle_and_alone(oracle, page):
     o, l = dev.run(batch, plan=plan)
     rows = sample_rows(batch, 24, seed=page)
     ro, rl = oracle_rows(oracle, work, batch, rows=rows)
-    assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"chains page {page}")
+    assert_close_to_oracle(o, l, ro, rl, rows=rows, what=f"chains {shape} page {page}")
     for i in (0, 2, 4):
         alone = wl.sub_batch(batch, work.prompts, page, [i])
         o_1, l_1 = dev.run(alone)
         a, b = int(batch.qo_indptr[i]), int(batch.qo_indptr[i + 1])
-        assert_bits_equal(o_1, o[a:b], f"page {page}: request {i} alone vs in the batch")
-        assert_bits_equal(l_1, l[a:b], f"page {page}: request {i} alone vs in the batch (lse)")
+        assert_bits_equal(o_1, o[a:b], f"{shape} page {page}: request {i} alone vs in the batch")
+        assert_bits_equal(l_1, l[a:b], f"{shape} page {page}: request {i} alone vs in the batch (lse)")
 
 
-def test_chained_and_unchained_launches_agree():
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_chained_and_unchained_launches_agree(shape):
     """One set of prompts placed with page size 16 (persistent launch, scalar descriptors),
     12 (persistent, per-lane general addressing) and 1 (one unit per workgroup): the outputs
     are bit-identical -- neither the chain a unit lands in nor the page layout enters a
     row's arithmetic."""
+    hq, hkv, d = SHAPES[shape]
     outs = {}
     for page in (16, 12, 1):
-        work = wl.random_workload(790, hq=32, hkv=8, d=128, page_size=page, kv_dtype="bf16", specs=SPECS)
+        work = wl.random_workload(790, hq=hq, hkv=hkv, d=d, page_size=page, kv_dtype="bf16", specs=SPECS)
         outs[page] = Device(work).run(work.batches["batch"])
     for page in (12, 1):
         assert_bits_equal(outs[page][0], outs[16][0], f"page {page} vs page 16")
@@ -68,12 +75,14 @@ def test_chained_and_unchained_launches_agree():
     assert np.isfinite(outs[16][0].float().numpy()).all()
 
 
-def test_chained_passes_under_a_workspace_cap():
+@pytest.mark.parametrize("shape", list(SHAPES))
+def test_chained_passes_under_a_workspace_cap(shape):
     """A cap small enough to cut the partial-holding tiles of a 9000-token prompt into several
     passes: every pass is its own persistent launch over its own unit records (plus a merge);
     the rows are bit-identical to the uncapped single pass."""
     specs = [(9000, 900), (1300, 1300), (600, 200)]
-    work = wl.random_workload(795, hq=32, hkv=8, d=128, page_size=16, kv_dtype="bf16", specs=specs)
+    hq, hkv, d = SHAPES[shape]
+    work = wl.random_workload(795, hq=hq, hkv=hkv, d=d, page_size=16, kv_dtype="bf16", specs=specs)
     dev = Device(work)
     batch = work.batches["batch"]
     free = dev.plan(batch)

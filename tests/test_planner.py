@@ -238,12 +238,18 @@ def test_persistent_chains_per_pass(dpp):
 
 
 def test_no_chains_where_not_persistent(dpp):
-    # narrow passes (extends), head_dim 256 and fp8 launches are not persistent
+    # narrow passes (extends), head_dim 512 (four waves) and fp8 launches are not persistent;
+    # wide bf16 passes at head_dim 256 (eight waves) are
     ext = _specs_batch([(1024 + t, t) for t in (1, 2, 3, 4)] * 4)
     assert len(parse(_plan(dpp, ext).header()).units) == 0
     big = _specs_batch([(1028, 1028)] * 2)
-    assert len(parse(_plan(dpp, big, hq=16, hkv=4, d=256).header()).units) == 0
+    assert len(parse(_plan(dpp, big, hq=16, hkv=4, d=512).header()).units) == 0
     assert len(parse(_plan(dpp, big, kv_dtype="fp8_e4m3", k_scale=1.0, v_scale=1.0).header()).units) == 0
+    assert len(parse(_plan(dpp, big, hq=16, hkv=4, d=256, kv_dtype="fp8_e4m3", k_scale=1.0,
+                           v_scale=1.0).header()).units) == 0
+    p256 = _plan(dpp, big, hq=16, hkv=4, d=256)
+    parsed = parse(p256.header())
+    _check_chains(parsed, parsed.items, parsed.units, 4)
     # page size 1: two page tables of a 4096-key split do not fit beside the ring
     assert len(parse(_plan(dpp, _specs_batch([(5000, 5000)], page=1), page=1).header()).units) == 0
 
