@@ -182,6 +182,11 @@ dpp_status launch_passes(const dpp_plan* plan, const void* q, const void* k_pool
       a.num_items = end - a.item_begin;
       a.chain_offset = narrow ? -1 : plan->chain_offset[(size_t)p];
       a.num_chains = narrow ? 0 : plan->chain_blocks[(size_t)p];
+      // A wide launch that is not persistent runs the planner's block table (cost-balanced
+      // XCD runs); the narrow launches run equal-count runs (xcd_chunked).
+      const bool table = !narrow && a.chain_offset < 0;
+      a.block_table = table ? plan->block_table_offset[(size_t)p] : -1;
+      a.table_blocks = table ? plan->block_table_blocks[(size_t)p] : 0;
       if (a.num_items > 0) {
         e = launch_prefill(a, plan->cfg.head_dim, plan->cfg.kv_dtype, narrow != 0, plan->block_n, stream);
         if (e != hipSuccess) return hip_fail(e, "prefill launch");

@@ -158,7 +158,8 @@ struct HeaderPreamble {
   int32_t zero_chunk[4];   // zero: the gather reads these 16 bytes in place of a missing chunk
   int32_t unit_offset;     // word offset of the unit records (all passes), 0 if none
   int32_t num_units;
-  int32_t reserved[2];     // zero
+  int32_t table_offset;    // word offset of the block tables (pass, blocks, entries...), 0 if none
+  int32_t num_tables;
 };
 static_assert(sizeof(HeaderPreamble) == kHeaderWords * 4, "preamble size");
 static_assert(offsetof(HeaderPreamble, zero_chunk) % 16 == 0, "zero chunk must be 16-byte aligned");
@@ -180,8 +181,8 @@ struct PrefillArgs {
   int32_t item_offset;      // word offset of the item records in the header
   int32_t item_begin;       // first item of this launch
   int32_t num_items;        // items in this launch
-  int32_t chain_offset;     // persistent launch: word offset of its unit records; -1: block b
-                            // runs unit xcd_chunked(b, num_items * num_kv_heads)
+  int32_t chain_offset;     // persistent launch: word offset of its unit records; -1: see
+                            // block_table
   int32_t num_chains;       // persistent launch: its workgroups (one per chain)
   int32_t num_qo_heads;
   int32_t num_kv_heads;
@@ -190,6 +191,10 @@ struct PrefillArgs {
   int32_t page_slots;       // entries of one unit's page-id table in LDS
   int32_t ragged;           // 1: K/V are [tokens, Hkv, D]; a request's page_start is its first
                             // token and its keys sit on one virtual page with id 0
+  int32_t block_table;      // wide launch that is not persistent: word offset of its block table
+                            // (block b runs unit table[b], or exits at -1); -1: block b runs unit
+                            // xcd_chunked(b, num_items * num_kv_heads)
+  int32_t table_blocks;     // entries of that table: the launch's workgroups
   float scale_log2;         // sm_scale * log2(e), rounded once to fp32
   float k_scale;
   float v_scale;

@@ -16,10 +16,10 @@
 //    together and longest first (load balance, and L2 reuse of the request's KV); a pass of
 //    tiles with at most kNarrowRows rows each runs on the narrow kernel;
 //  * persistent chains: a wide bf16 pass at head_dim <= 256 runs as kPersistentBlocks
-//    workgroups, each over a chain of units (item, kv head). The units that the plain launch
-//    order would send to XCD x (a contiguous run, see xcd_chunked) are dealt longest first
-//    to the least loaded of the workgroups on XCD x (b % kXcds == x), each chain then
-//    rotated by the workgroup's rank on its XCD. Order, passes, cap,
+//    workgroups, each over a chain of units (item, kv head). XCD x takes a contiguous run of
+//    the plain launch order (unit kv_head * items + item) holding its share of the pass's
+//    cost; the run is dealt longest first to the least loaded of the workgroups on XCD x
+//    (b % kXcds == x), each chain then rotated by the workgroup's rank on its XCD. Order, passes, cap,
 //    chains and kernel instantiation change when and where a row is computed, never its
 //    arithmetic.
 #include "plan.h"
@@ -55,6 +55,72 @@ struct TileInfo {
   int64_t slot_base = -1;
 };
 
+// Cost of a unit (item, kv head) for load balance: its KV tiles plus a start-up allowance.
+int64_t unit_cost(const PrefillItem& it) { return (int64_t)(it.kv_tile_end - it.kv_tile_begin) + kUnitOverheadTiles; }
+
+// XCD groups: kXcdGroup neighbouring XCDs (x / kXcdGroup == g) share one run of the plain
+// launch order (unit w = kv_head * n + item, the n items of one wide launch): group g takes
+// units [run[g], run[g+1]), a contiguous run (so that the units of one kv head share few L2s)
+// holding its share of the total cost. With `blocks` > 0 the shares follow the workgroups
+// b < blocks of each group and every run holds at least one unit per workgroup; otherwise the
+// shares are equal. Runs of equal unit counts per XCD would not balance (with 4 kv heads on 8
+// XCDs, one XCD of each pair would take the long tiles of its head and the other the short
+// ones), and a run per single XCD leaves it units of one size, which its compute units cannot
+// share out evenly; a pair of XCDs deals the long and the short units of its run between them.
+constexpr int kXcdGroup = 2;
+constexpr int kGroups = kXcds / kXcdGroup;
+std::vector<int64_t> group_runs(const PrefillItem* items, int32_t n, int32_t num_kv_heads, int32_t blocks) {
+  const int64_t n_units = (int64_t)n * num_kv_heads;
+  std::vector<int64_t> prefix((size_t)n_units + 1, 0);
+  for (int64_t u = 0; u < n_units; ++u) prefix[(size_t)u + 1] = prefix[(size_t)u] + unit_cost(items[u % n]);
+  auto blocks_of = [&](int g) {  // workgroups b < blocks with b % kXcds in group g
+    int64_t c = 0;
+    for (int x = g * kXcdGroup; x < (g + 1) * kXcdGroup; ++x) c += blocks > x ? (blocks - 1 - x) / kXcds + 1 : 0;
+    return c;
+  };
+  std::vector<int64_t> run((size_t)kGroups + 1, 0);
+  const int64_t weight_total = blocks > 0 ? blocks : kGroups;
+  int64_t weight_before = 0, start = 0;
+  for (int g = 0; g < kGroups; ++g) {
+    const int64_t bg = blocks > 0 ? blocks_of(g) : 0;
+    weight_before += blocks > 0 ? bg : 1;
+    const int64_t min_after = blocks > 0 ? blocks - weight_before : 0;
+    int64_t e = n_units;
+    if (g < kGroups - 1) {
+      // the first end whose prefix reaches the target, or the one before it if that is closer
+      const int64_t target = (prefix[(size_t)n_units] * weight_before + weight_total / 2) / weight_total;
+      e = std::lower_bound(prefix.begin() + start, prefix.end(), target) - prefix.begin();
+      if (e > start && target - prefix[(size_t)e - 1] < prefix[(size_t)std::min<int64_t>(e, n_units)] - target) --e;
+      e = std::min(std::max(e, start + bg), n_units - min_after);
+    }
+    run[(size_t)g + 1] = e;
+    start = e;
+  }
+  return run;
+}
+
+// Block table of a wide launch that is not persistent: entry b (block b, which the dispatcher
+// hands to XCD b % kXcds) is the unit that block runs, or -1 (the block exits). Group g's run,
+// longest first, is dealt round-robin to its XCDs, so every XCD starts its longest units first
+// and its compute units fill in behind them with the short ones.
+std::vector<int32_t> block_table(const PrefillItem* items, int32_t n, int32_t num_kv_heads) {
+  const std::vector<int64_t> run = group_runs(items, n, num_kv_heads, 0);
+  std::vector<std::vector<int32_t>> per_xcd(kXcds);
+  for (int g = 0; g < kGroups; ++g) {
+    std::vector<int64_t> order;
+    for (int64_t u = run[(size_t)g]; u < run[(size_t)g + 1]; ++u) order.push_back(u);
+    std::stable_sort(order.begin(), order.end(),
+                     [&](int64_t a, int64_t b) { return unit_cost(items[a % n]) > unit_cost(items[b % n]); });
+    for (size_t r = 0; r < order.size(); ++r) per_xcd[(size_t)g * kXcdGroup + r % kXcdGroup].push_back((int32_t)order[r]);
+  }
+  size_t len = 0;
+  for (const auto& l : per_xcd) len = std::max(len, l.size());
+  std::vector<int32_t> table(len * kXcds, -1);
+  for (int x = 0; x < kXcds; ++x)
+    for (size_t k = 0; k < per_xcd[(size_t)x].size(); ++k) table[k * kXcds + (size_t)x] = per_xcd[(size_t)x][k];
+  return table;
+}
+
 // Largest slot count n with align(n*D*4) + align(n*4) <= avail.
 // Persistent chains of one wide pass whose units are (item i, kv head h), unit w = h * n + i
 // for the n items at `items`: records placed so that workgroup b starts at record b.
@@ -64,18 +130,16 @@ std::vector<UnitRecord> build_chains(const PrefillItem* items, int32_t n, int32_
   const int32_t nb = (int32_t)std::min<int64_t>(n_units, kPersistentBlocks);
   std::vector<UnitRecord> rec((size_t)n_units);
   int32_t next_free = nb;
-  const int64_t q = n_units / kXcds, r = n_units % kXcds;
-  for (int x = 0; x < kXcds; ++x) {
-    const int64_t u0 = x * q + std::min<int64_t>(x, r), len = q + (x < r ? 1 : 0);
+  auto cost = [&](int64_t u) { return unit_cost(items[u % n]); };
+  const std::vector<int64_t> run_begin = group_runs(items, n, num_kv_heads, nb);
+  for (int g = 0; g < kGroups; ++g) {
+    const int64_t u0 = run_begin[(size_t)g], len = run_begin[(size_t)g + 1] - u0;
     std::vector<int32_t> blocks;
-    for (int32_t b = x; b < nb; b += kXcds) blocks.push_back(b);
+    for (int32_t b = 0; b < nb; ++b)
+      if ((b % kXcds) / kXcdGroup == g) blocks.push_back(b);
     if (len == 0) continue;
     std::vector<int64_t> order((size_t)len);
     for (int64_t k = 0; k < len; ++k) order[(size_t)k] = u0 + k;
-    auto cost = [&](int64_t u) {
-      const PrefillItem& it = items[u % n];
-      return (int64_t)(it.kv_tile_end - it.kv_tile_begin) + kUnitOverheadTiles;
-    };
     std::stable_sort(order.begin(), order.end(), [&](int64_t a, int64_t b) { return cost(a) > cost(b); });
     std::vector<int64_t> load(blocks.size(), 0);
     std::vector<std::vector<int64_t>> chain(blocks.size());
@@ -87,8 +151,8 @@ std::vector<UnitRecord> build_chains(const PrefillItem* items, int32_t n, int32_
       chain[k].push_back(u);
     }
     // A workgroup's finish time is the sum over its chain, whatever the order; rotating the
-    // j-th workgroup's chain by j keeps neighbours from switching units (a burst of Q reads
-    // and O writes) at the same moments.
+    // j-th workgroup's chain (of its group) by j keeps neighbours from switching units (a
+    // burst of Q reads and O writes) at the same moments.
     for (size_t k = 0; k < blocks.size(); ++k) {
       std::vector<int64_t>& c = chain[k];
       if (c.empty()) continue;
@@ -246,7 +310,12 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
   // Unit records of persistent launches: at most one per (item, kv head).
   const bool chain_kind = chained_launch(c.head_dim, c.kv_dtype == DPP_KV_FP8_E4M3, false);
   const int64_t max_units = chain_kind ? n_items * c.num_kv_heads : 0;
-  const int64_t words_max = kHeaderWords + 4 * (int64_t)batch_size + kItemWords * (n_items + max_units) + 4 * n_merges;
+  // block tables of the wide launches that are not persistent: per pass 2 words and kXcds
+  // entries per unit of the longest XCD list, at most half a group's run (a persistent kind
+  // that falls back to tables needs fewer words than its unit records would)
+  const int64_t max_table_words = chain_kind ? 0 : 4 * n_items * c.num_kv_heads + (2 + kXcds) * n_items;
+  const int64_t words_max =
+      kHeaderWords + 4 * (int64_t)batch_size + kItemWords * (n_items + max_units) + 4 * n_merges + max_table_words;
   if (words_max > std::numeric_limits<int32_t>::max() / 2)
     return fail(DPP_ERR_UNSUPPORTED, "batch too large for one plan");
   // The cap is checked against the largest header this plan can have (its unit records
@@ -388,10 +457,29 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
     plan->chain_blocks[(size_t)p] = (int32_t)std::min<int64_t>(r.size(), kPersistentBlocks);
     units.insert(units.end(), r.begin(), r.end());
   }
-  const int64_t words = unit_offset + kItemWords * (int64_t)units.size();
+  // Block tables of the wide launches that are not persistent, after the unit records: per
+  // pass, its index and block count, then the entries.
+  const int32_t table_offset = unit_offset + kItemWords * (int32_t)units.size();
+  std::vector<int32_t> tables;
+  int32_t num_tables = 0;
+  plan->block_table_offset.assign((size_t)num_passes, -1);
+  plan->block_table_blocks.assign((size_t)num_passes, 0);
+  for (int32_t p = 0; p < num_passes; ++p) {
+    const int32_t b0 = plan->item_pass[(size_t)p], b1 = plan->item_narrow[(size_t)p];
+    if (b1 <= b0 || plan->chain_offset[(size_t)p] >= 0) continue;
+    const std::vector<int32_t> t = block_table(items.data() + b0, b1 - b0, c.num_kv_heads);
+    tables.push_back(p);
+    tables.push_back((int32_t)t.size());
+    plan->block_table_offset[(size_t)p] = table_offset + (int32_t)tables.size();
+    plan->block_table_blocks[(size_t)p] = (int32_t)t.size();
+    tables.insert(tables.end(), t.begin(), t.end());
+    ++num_tables;
+  }
+  const int64_t words = table_offset + (int64_t)tables.size();
+  if (words > words_max) return fail(DPP_ERR_INVALID, "internal error: work list longer than its bound");
   const size_t header_bytes = align_up((size_t)words * 4, 256);
 
-  // Serialise: preamble | requests | items | merges | unit records.
+  // Serialise: preamble | requests | items | merges | unit records | block tables.
   plan->header.assign((size_t)words, 0);
   HeaderPreamble pre{};
   pre.magic = kHeaderMagic;
@@ -403,6 +491,8 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
   pre.merge_offset = pre.item_offset + kItemWords * (int32_t)n_items;
   pre.unit_offset = units.empty() ? 0 : unit_offset;
   pre.num_units = (int32_t)units.size();
+  pre.table_offset = tables.empty() ? 0 : table_offset;
+  pre.num_tables = num_tables;
   {
     // ids differ between plans of one process; mixing in the address makes a header left
     // behind by another process unlikely to match either
@@ -421,6 +511,7 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
     std::memcpy(plan->header.data() + pre.merge_offset, merges.data(), merges.size() * sizeof(MergeItem));
   if (!units.empty())
     std::memcpy(plan->header.data() + unit_offset, units.data(), units.size() * sizeof(UnitRecord));
+  if (!tables.empty()) std::memcpy(plan->header.data() + table_offset, tables.data(), tables.size() * sizeof(int32_t));
 
   plan->max_partial_slots = max_used;
   plan->header_bytes = header_bytes;

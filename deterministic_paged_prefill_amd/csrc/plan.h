@@ -33,6 +33,10 @@ struct dpp_plan {
   // over the unit records at that word offset of the header.
   std::vector<int32_t> chain_offset;
   std::vector<int32_t> chain_blocks;
+  // Pass p's wide launch when it is not persistent: block_table_blocks[p] workgroups, block b
+  // running the unit at word block_table_offset[p] + b of the header (-1: none).
+  std::vector<int32_t> block_table_offset;
+  std::vector<int32_t> block_table_blocks;
 
   int64_t max_partial_slots = 0;
   size_t header_bytes = 0;

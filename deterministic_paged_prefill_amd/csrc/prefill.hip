@@ -37,6 +37,7 @@
 // arithmetic.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <climits>
 #include <cstdint>
@@ -269,10 +270,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 
   // ---- the unit (item, kv head) record: word k in lane k of one register, read into scalar
   // registers by decode. A persistent launch starts workgroup b at record b of its chain
-  // records; otherwise work w = kvh * num_items + item goes to block b with w =
-  // xcd_chunked(b, n): the dispatcher hands block b to XCD b % kXcds, and each XCD then
-  // receives one contiguous range of w (the q tiles that read one request's KV for one kv
-  // head share an L2).
+  // records; otherwise work w = kvh * num_items + item goes to block b (which the dispatcher
+  // hands to XCD b % kXcds): in a wide launch the planner's block table names it (each pair
+  // of XCDs a contiguous range of w of equal cost, longest units first; a block without a
+  // unit exits at once), in a narrow one w = xcd_chunked(b, n) (each XCD one contiguous range
+  // of equal count). Contiguous ranges keep the q tiles that read one request's KV for one kv
+  // head, and the two workgroups of a head_dim-split unit, on few L2s.
   const HeaderPreamble* pre = reinterpret_cast<const HeaderPreamble*>(a.header);
   const bool chained = a.chain_offset >= 0;
   auto fetch_record = [&](int idx) -> int32_t {
@@ -287,7 +290,13 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     // VH: the two workgroups of a unit are work indices 2u and 2u + 1, so that both usually
     // fall in one XCD's range and share its L2 for K
     const int nw = a.num_items * a.num_kv_heads;
-    int w = xcd_chunked(blockIdx.x, VH ? 2 * nw : nw);
+    int w;
+    if (!VH && a.block_table >= 0) {
+      w = a.header[a.block_table + blockIdx.x];
+      if (w < 0 || w >= nw) return;  // no unit for this block (uniform: before any wait)
+    } else {
+      w = xcd_chunked(blockIdx.x, VH ? 2 * nw : nw);
+    }
     if constexpr (VH) {
       vh = w & 1;
       w >>= 1;
@@ -1198,7 +1207,10 @@ hipError_t launch_one(const PrefillArgs& a, hipStream_t stream) {
     lds_opt_in = (int)lds;
   }
   if (VH && a.chain_offset >= 0) return hipErrorInvalidValue;
-  dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains : (VH ? 2 : 1) * a.num_items * a.num_kv_heads));
+  if (a.block_table >= 0 && (VH || a.table_blocks < a.num_items * a.num_kv_heads)) return hipErrorInvalidValue;
+  dim3 grid((unsigned)(a.chain_offset >= 0 ? a.num_chains
+                       : a.block_table >= 0 ? a.table_blocks
+                                            : (VH ? 2 : 1) * a.num_items * a.num_kv_heads));
   if (a.chain_offset >= 0 && !chained_launch(D, FP8, NARROW)) return hipErrorInvalidValue;
   hipLaunchKernelGGL((prefill_kernel<D, FP8, NB, NARROW, MODE, VH, BNX>), grid, dim3(C::THREADS), lds, stream, a);
   return hipGetLastError();

@@ -15,6 +15,8 @@ class ParsedPlan:
     merges: np.ndarray    # [M, 4]: request, row_start, tile_splits, slot_base
     units: np.ndarray     # [U, 16]: persistent launches' unit records: the item's first 7 words,
                           # next, the request's 4 words, kv_head, block, pass, pad
+    tables: dict          # pass -> block table of its wide launch when not persistent: entry b is
+                          # the unit (kv_head * items + item) block b runs, -1 none
 
 
 def parse(words: np.ndarray) -> ParsedPlan:
@@ -24,7 +26,14 @@ def parse(words: np.ndarray) -> ParsedPlan:
     req = w[roff:roff + 4 * nreq].reshape(nreq, 4)
     items = w[ioff:ioff + 16 * nitems].reshape(nitems, 16)
     merges = w[moff:moff + 4 * nmerge].reshape(nmerge, 4)
-    assert (w[8:12] == 0).all() and (w[14:16] == 0).all(), "zero chunk and reserved words"
+    assert (w[8:12] == 0).all(), "zero chunk"
     uoff, nunits = int(w[12]), int(w[13])
     units = w[uoff:uoff + 16 * nunits].reshape(nunits, 16)
-    return ParsedPlan(req, items, merges, units)
+    toff, ntables = int(w[14]), int(w[15])
+    tables = {}
+    for _ in range(ntables):
+        ps, blocks = int(w[toff]), int(w[toff + 1])
+        tables[ps] = w[toff + 2:toff + 2 + blocks]
+        toff += 2 + blocks
+    assert toff == len(w) or ntables == 0, "block tables end the work list"
+    return ParsedPlan(req, items, merges, units, tables)

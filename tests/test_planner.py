@@ -170,6 +170,13 @@ def test_cap_bounds_workspace_and_adds_passes(dpp, cap_mib):
     assert sorted(map(key, parse(p.header()).items)) == sorted(map(key, parse(unbounded.header()).items))
 
 
+XCD_GROUP = 2  # neighbouring XCDs that share one run of the plain launch order
+
+
+def _group_of(b, xcds=8):
+    return (b % xcds) // XCD_GROUP
+
+
 def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
     """The unit records of one persistent launch over `items` (its pass's items, launch order)."""
     n = len(items)
@@ -181,6 +188,7 @@ def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
     seen = np.zeros(n_units, dtype=bool)
     covered = set()
     load = {}
+    group_units = {}
     for b in range(nb):
         assert units[b][13] == b, "workgroup b starts at record b"
         k, costs = b, []
@@ -192,10 +200,7 @@ def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
             i = index[tuple(int(x) for x in rec[:3])]
             assert (rec[:7] == items[i][:7]).all() and (rec[8:12] == items[i][8:12]).all()
             h = int(rec[12])
-            w = h * n + i
-            q, r = divmod(n_units, xcds)
-            x = next(x for x in range(xcds) if x * q + min(x, r) <= w < x * q + min(x, r) + q + (x < r))
-            assert b % xcds == x, "a unit runs on the XCD the plain launch order gives it"
+            group_units.setdefault(_group_of(b, xcds), []).append(h * n + i)  # plain launch order
             covered.add((i, h))
             c = cost(rec)
             costs.append(c)
@@ -207,10 +212,56 @@ def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
     assert seen.all(), "every record is on a chain"
     assert covered == {(i, h) for i in range(n) for h in range(hkv)}
     biggest = max(cost(u) for u in units)
-    for x in range(xcds):
-        loads = [load[b] for b in range(x, nb, xcds)]
+    groups = xcds // XCD_GROUP
+    members = {g: [b for b in range(nb) if _group_of(b, xcds) == g] for g in range(groups)}
+    for g in range(groups):
+        loads = [load[b] for b in members[g]]
         if loads:
             assert max(loads) - min(loads) <= biggest
+    # group g holds a contiguous run of the plain order, the runs in group order, and its share
+    # of the cost in proportion to its workgroups (within the largest units, unless its run is
+    # pinned at one unit per workgroup)
+    total = sum(load.values())
+    start = 0
+    for g in range(groups):
+        run = sorted(group_units.get(g, []))
+        assert run == list(range(start, start + len(run))), "contiguous runs in group order"
+        start += len(run)
+        bg = len(members[g])
+        assert len(run) >= bg, "a unit for every workgroup"
+        share = total * bg / nb
+        got = sum(load[b] for b in members[g])
+        assert abs(got - share) <= 2 * biggest or len(run) == bg, (g, got, share)
+    assert start == n_units
+
+
+def _check_table(table, items, hkv, xcds=8):
+    """The block table of a wide launch that is not persistent over `items`."""
+    n = len(items)
+    n_units = n * hkv
+    t = np.asarray(table)
+    assert len(t) % xcds == 0 and len(t) >= n_units
+    used = t[t >= 0]
+    assert sorted(used.tolist()) == list(range(n_units)), "every unit once"
+    cost = np.array([int(items[u % n][5] - items[u % n][4]) + 2 for u in range(n_units)])
+    groups = xcds // XCD_GROUP
+    start = 0
+    per_xcd = np.zeros(xcds)
+    for g in range(groups):
+        blocks = [b for b in range(len(t)) if _group_of(b, xcds) == g and t[b] >= 0]
+        run = sorted(int(t[b]) for b in blocks)
+        assert run == list(range(start, start + len(run))), "contiguous runs in group order"
+        start += len(run)
+        for x in range(g * XCD_GROUP, (g + 1) * XCD_GROUP):
+            mine = [int(t[b]) for b in range(x, len(t), xcds)]
+            live = [w for w in mine if w >= 0]
+            assert mine[:len(live)] == live, "an XCD's blocks without a unit come last"
+            assert all(cost[a] >= cost[b] for a, b in zip(live, live[1:])), "longest first"
+            per_xcd[x] = cost[live].sum() if live else 0
+    assert start == n_units
+    if n_units >= 8 * xcds:
+        biggest = cost.max()
+        assert per_xcd.max() - per_xcd.mean() <= 2 * biggest + 0.05 * per_xcd.mean(), per_xcd
 
 
 @pytest.mark.parametrize("specs", [[(1028, 1028)] * 16, [(67, 67)], [(1028, 1028)] * 2,
@@ -220,6 +271,67 @@ def test_persistent_chains_cover_every_unit_once(dpp, specs):
     parsed = parse(_plan(dpp, _specs_batch(specs)).header())
     assert (parsed.units[:, 14] == 0).all()
     _check_chains(parsed, parsed.items, parsed.units, 8)
+
+
+def test_persistent_chains_balance_xcds_at_four_kv_heads(dpp):
+    # 4 kv heads on 8 XCDs: equal-count runs of the plain order would give one XCD of each pair
+    # the long tiles of its head and the other the short ones (1.42 : 0.58 at 8,192 tokens)
+    for specs in ([(8192, 8192)], [(32768, 32768)], [(3000, 3000), (200, 200)] * 3):
+        p = _plan(dpp, _specs_batch(specs, g=6), hq=24, hkv=4, d=256, cap=256 << 20)
+        parsed = parse(p.header())
+        for ps in range(p.info.num_passes):
+            units = parsed.units[parsed.units[:, 14] == ps]
+            items = parsed.items[parsed.items[:, 7] == ps]
+            _check_chains(parsed, items, units, 4)
+            cost = (units[:, 5] - units[:, 4]) + 2
+            per_xcd = np.bincount(units[:, 13] % 8, weights=cost, minlength=8)
+            assert per_xcd.max() <= 1.05 * per_xcd.mean(), per_xcd
+
+
+@pytest.mark.parametrize("kind", ["fp8_d256", "fp8_d128", "bf16_d512", "bf16_d128_page1"])
+def test_block_tables_of_wide_launches(dpp, kind):
+    # wide launches that are not persistent (fp8, head_dim 512, page size 1 where two page
+    # tables do not fit) run a block table: every unit once, contiguous cost-balanced runs per
+    # pair of XCDs, each XCD's units longest first; persistent and narrow launches have none
+    fp8 = dict(kv_dtype="fp8_e4m3", k_scale=1.0, v_scale=1.0)
+    hq, hkv, d, page, kw = {"fp8_d256": (24, 4, 256, 16, fp8), "fp8_d128": (32, 8, 128, 16, fp8),
+                            "bf16_d512": (16, 4, 512, 16, {}), "bf16_d128_page1": (32, 8, 128, 1, {})}[kind]
+    for specs in ([(8192, 8192)], [(2048, 2048)] * 4, [(9000, 900), (1300, 1300), (600, 200)], [(67, 67)],
+                  [(32768, 32768)]):
+        if page == 1 and specs[0][0] > 9000:
+            continue
+        p = _plan(dpp, _specs_batch(specs, page=page, g=hq // hkv), hq=hq, hkv=hkv, d=d, page=page,
+                  cap=64 << 20, **kw)
+        parsed = parse(p.header())
+        if kind != "bf16_d128_page1":
+            assert len(parsed.units) == 0
+        for ps in range(p.info.num_passes):
+            items = parsed.items[parsed.items[:, 7] == ps]
+            if ps in parsed.tables:
+                assert not (parsed.units[:, 14] == ps).any()
+                _check_table(parsed.tables[ps], items, hkv)
+            else:  # page size 1 with units short enough for two page tables: persistent
+                _check_chains(parsed, items, parsed.units[parsed.units[:, 14] == ps], hkv)
+        if kind == "bf16_d128_page1" and specs[0][0] > 4200:
+            assert parsed.tables, "a unit spanning 4096 one-token pages needs the one-table launch"
+    ext = _specs_batch([(1024 + t, t) for t in range(1, 16 // (hq // hkv) + 1)] * 4, page=page, g=hq // hkv)
+    assert parse(_plan(dpp, ext, hq=hq, hkv=hkv, d=d, page=page, **kw).header()).tables == {}
+
+
+def test_block_tables_balance_xcds(dpp):
+    # the fp8 24/4/256 prefill of 8,192 tokens: equal-count XCD runs put 1.42x the mean cost on
+    # half the XCDs; the table's per-XCD costs are within 2 % of the mean
+    p = _plan(dpp, _specs_batch([(8192, 8192)], g=6), hq=24, hkv=4, d=256, kv_dtype="fp8_e4m3", k_scale=1.0,
+              v_scale=1.0)
+    parsed = parse(p.header())
+    t = parsed.tables[0]
+    cost = (parsed.items[:, 5] - parsed.items[:, 4]) + 2
+    n = len(parsed.items)
+    per_xcd = np.zeros(8)
+    for b, w in enumerate(t):
+        if w >= 0:
+            per_xcd[b % 8] += cost[w % n]
+    assert per_xcd.max() <= 1.02 * per_xcd.mean(), per_xcd
 
 
 def test_persistent_chains_per_pass(dpp):
