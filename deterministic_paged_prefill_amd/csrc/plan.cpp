@@ -121,6 +121,53 @@ std::vector<int32_t> block_table(const PrefillItem* items, int32_t n, int32_t nu
   return table;
 }
 
+// Lowers the largest chain load of a group left by the longest-first dealing: while a move of
+// one unit of the most loaded chain to another chain, or a swap with a shorter unit there,
+// lowers the larger of the two loads below the maximum, make the best such change (ties: the
+// first found). Bounded; deterministic.
+template <class Cost>
+void refine_chains(std::vector<std::vector<int64_t>>& chain, std::vector<int64_t>& load, const Cost& cost) {
+  const size_t nb = chain.size();
+  if (nb < 2) return;
+  for (size_t iter = 0; iter < 4 * nb; ++iter) {
+    size_t m = 0;
+    for (size_t j = 1; j < nb; ++j)
+      if (load[j] > load[m]) m = j;
+    const int64_t M = load[m];
+    int64_t best = M;
+    size_t bi = 0, bb = 0, bj = 0;
+    bool found = false, swap = false;
+    for (size_t i = 0; i < chain[m].size(); ++i) {
+      const int64_t cu = cost(chain[m][i]);
+      for (size_t b = 0; b < nb; ++b) {
+        if (b == m) continue;
+        const int64_t moved = std::max(load[b] + cu, M - cu);
+        if (moved < best) { best = moved; bi = i; bb = b; found = true; swap = false; }
+        for (size_t j = 0; j < chain[b].size(); ++j) {
+          const int64_t cv = cost(chain[b][j]);
+          if (cv >= cu) continue;
+          const int64_t swapped = std::max(M - cu + cv, load[b] - cv + cu);
+          if (swapped < best) { best = swapped; bi = i; bb = b; bj = j; found = true; swap = true; }
+        }
+      }
+    }
+    if (!found) return;
+    const int64_t u = chain[m][bi], cu = cost(u);
+    if (swap) {
+      const int64_t v = chain[bb][bj], cv = cost(v);
+      chain[m][bi] = v;
+      chain[bb][bj] = u;
+      load[m] += cv - cu;
+      load[bb] += cu - cv;
+    } else {
+      chain[m].erase(chain[m].begin() + (std::ptrdiff_t)bi);
+      chain[bb].push_back(u);
+      load[m] -= cu;
+      load[bb] += cu;
+    }
+  }
+}
+
 // Largest slot count n with align(n*D*4) + align(n*4) <= avail.
 // Persistent chains of one wide pass whose units are (item i, kv head h), unit w = h * n + i
 // for the n items at `items`: records placed so that workgroup b starts at record b.
@@ -150,6 +197,9 @@ std::vector<UnitRecord> build_chains(const PrefillItem* items, int32_t n, int32_
       load[k] += cost(u);
       chain[k].push_back(u);
     }
+    refine_chains(chain, load, cost);
+    for (auto& c : chain)  // longest first again (the refinement moves units between chains)
+      std::stable_sort(c.begin(), c.end(), [&](int64_t a, int64_t b) { return cost(a) > cost(b) || (cost(a) == cost(b) && a < b); });
     // A workgroup's finish time is the sum over its chain, whatever the order; rotating the
     // j-th workgroup's chain (of its group) by j keeps neighbours from switching units (a
     // burst of Q reads and O writes) at the same moments.
