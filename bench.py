@@ -154,12 +154,13 @@ class Runner:
             up_t.append(t2 - t1)
         return float(np.median(plan_t) * 1e6), float(np.median(up_t) * 1e6)
 
-    def stream_timed(self, split: int, depth: int, steps: int, warmup: int) -> float:
+    def stream_timed(self, split: int, depth: int, steps: int, warmup: int, head_split: bool = False) -> float:
         """ms per launch of the read-only streaming reference (dpp_stream_kv) over the same pages,
         rotated like the attention steps."""
         import torch
+        flags = self.dpp.RUN_REUSE_UPLOAD | (self.dpp.STREAM_HEAD_SPLIT if head_split else 0)
         args = [(self.plan._h, self.k.data_ptr(), self.v.data_ptr(), self.k.shape[0], kvi.data_ptr(),
-                 kvi.numel(), self.ws.data_ptr(), self.ws.numel(), split, depth, self.dpp.RUN_REUSE_UPLOAD,
+                 kvi.numel(), self.ws.data_ptr(), self.ws.numel(), split, depth, flags,
                  self.stream.cuda_stream) for kvi in self.kvi]
         for i in range(warmup):
             self.dpp._check(self.lib.dpp_stream_kv(*args[i % self.replicas]))
@@ -172,7 +173,7 @@ class Runner:
         torch.cuda.synchronize()
         return start.elapsed_time(end) / steps
 
-    def stream_ceiling(self, steps: int, warmup: int) -> dict:
+    def stream_ceiling(self, steps: int, warmup: int, same_gather: bool = False) -> dict:
         """Best of the streaming reference's grids (1 or 2 workgroups per unit, 4 or 8 loads in
         flight per wave): the measured ceiling of this gather on this GPU."""
         best = None
@@ -181,7 +182,13 @@ class Runner:
                 ms = self.stream_timed(split, depth, steps, warmup)
                 if best is None or ms < best[0]:
                     best = (ms, split, depth)
-        return dict(ms=best[0], split=best[1], depth=best[2])
+        # the gather of the head_dim-split attention launch itself: two workgroups per unit, each
+        # all of K and half of V
+        out = dict(ms=best[0], split=best[1], depth=best[2])
+        if same_gather:
+            same = min((self.stream_timed(2, depth, steps, warmup, head_split=True), depth) for depth in (4, 8))
+            out.update(same_gather_ms=same[0], same_gather_depth=same[1])
+        return out
 
     def graph_timed(self, steps_per_graph: int, replays: int):
         """The same steps captured in one HIP graph (torch.cuda.graph over dpp_run, work list
@@ -383,7 +390,7 @@ def main() -> int:
         log(f"cached-vs-full max|diff| = {max_diff}")
         ms, wall = run.timed(args.steps, args.warmup)
         ms_graph = run.graph_timed(40, 10)
-        ceiling = run.stream_ceiling(args.steps, args.warmup)
+        ceiling = run.stream_ceiling(args.steps, args.warmup, same_gather=True)
         replan = run.replan_us()
         nbytes = kv_bytes(cached, hkv, d, 2)
         io_bytes = (2 * cached.num_q_tokens * hq * d * 2 + cached.num_q_tokens * hq * 4
@@ -554,7 +561,13 @@ def main() -> int:
                          "kv_gbps": round(ext["kv_bytes"] / (ext["ceiling"]["ms"] * 1e-3) / 1e9, 1),
                          "workgroups_per_unit": ext["ceiling"]["split"],
                          "loads_in_flight_per_wave": ext["ceiling"]["depth"],
-                         "frac": round(ext["ceiling"]["ms"] / ext["ms"], 4)}},
+                         "frac": round(ext["ceiling"]["ms"] / ext["ms"], 4),
+                         "same_gather": {
+                             "what": "the same reference reading what the attention launch reads: two "
+                                     "workgroups per unit, each all of K and one head_dim half of V",
+                             "us_per_launch": round(ext["ceiling"]["same_gather_ms"] * 1e3, 2),
+                             "loads_in_flight_per_wave": ext["ceiling"]["same_gather_depth"],
+                             "frac": round(ext["ceiling"]["same_gather_ms"] / ext["ms"], 4)}}},
         "extend_detail": {"us_per_step": round(ext["ms"] * 1e3, 2),
                           "host_wall_us_per_step": round(ext["wall_ms"] * 1e3, 2),
                           "graph_replay_us_per_step": round(ext["graph_ms"] * 1e3, 2),

@@ -38,6 +38,7 @@ def tile_shape(head_dim: int) -> tuple:
 
 DPP_OK, DPP_ERR_INVALID, DPP_ERR_SHAPE, DPP_ERR_UNSUPPORTED, DPP_ERR_WORKSPACE, DPP_ERR_HIP = range(6)
 RUN_REUSE_UPLOAD = 1
+STREAM_HEAD_SPLIT = 2  # dpp_stream_kv: two workgroups per unit split V's head_dim, as the narrow launch does
 PLAN_ADAPTIVE_KV_TILE = 1  # comparison mode: NOT batch invariant (see include/dpp.h)
 PLAN_PERMUTE_WORK = 2      # test mode: work order shuffled with the seed in bits 16..31
 KV_DTYPES = {"bf16": 0, "fp8_e4m3": 1}

@@ -16,12 +16,14 @@
 //    together and longest first (load balance, and L2 reuse of the request's KV); a pass of
 //    tiles with at most kNarrowRows rows each runs on the narrow kernel;
 //  * persistent chains: a wide bf16 pass at head_dim <= 256 runs as kPersistentBlocks
-//    workgroups, each over a chain of units (item, kv head). XCD x takes a contiguous run of
-//    the plain launch order (unit kv_head * items + item) holding its share of the pass's
-//    cost; the run is dealt longest first to the least loaded of the workgroups on XCD x
-//    (b % kXcds == x), each chain then rotated by the workgroup's rank on its XCD. Order, passes, cap,
-//    chains and kernel instantiation change when and where a row is computed, never its
-//    arithmetic.
+//    workgroups, each over a chain of units (item, kv head). Each group of XCDs (as many as
+//    share one kv head's units) takes a contiguous run of the plain launch order (unit
+//    kv_head * items + item) holding its share of the pass's cost; the run is dealt longest
+//    first to the least loaded of the group's workgroups (b % kXcds in the group), each chain
+//    then rotated by its workgroup's rank in the group;
+//  * block tables: a wide pass that is not persistent gets each group's run, longest first,
+//    dealt round-robin over the group's XCDs. Order, passes, cap, chains, tables and kernel
+//    instantiation change when and where a row is computed, never its arithmetic.
 #include "plan.h"
 
 #include <algorithm>
@@ -58,35 +60,41 @@ struct TileInfo {
 // Cost of a unit (item, kv head) for load balance: its KV tiles plus a start-up allowance.
 int64_t unit_cost(const PrefillItem& it) { return (int64_t)(it.kv_tile_end - it.kv_tile_begin) + kUnitOverheadTiles; }
 
-// XCD groups: kXcdGroup neighbouring XCDs (x / kXcdGroup == g) share one run of the plain
-// launch order (unit w = kv_head * n + item, the n items of one wide launch): group g takes
-// units [run[g], run[g+1]), a contiguous run (so that the units of one kv head share few L2s)
-// holding its share of the total cost. With `blocks` > 0 the shares follow the workgroups
-// b < blocks of each group and every run holds at least one unit per workgroup; otherwise the
-// shares are equal. Runs of equal unit counts per XCD would not balance (with 4 kv heads on 8
-// XCDs, one XCD of each pair would take the long tiles of its head and the other the short
-// ones), and a run per single XCD leaves it units of one size, which its compute units cannot
-// share out evenly; a pair of XCDs deals the long and the short units of its run between them.
-constexpr int kXcdGroup = 2;
-constexpr int kGroups = kXcds / kXcdGroup;
-std::vector<int64_t> group_runs(const PrefillItem* items, int32_t n, int32_t num_kv_heads, int32_t blocks) {
+// XCD groups: xg neighbouring XCDs (x / xg == g) share one run of the plain launch order
+// (unit w = kv_head * n + item, the n items of one wide launch): group g takes units
+// [run[g], run[g+1]), a contiguous run (so that the units of one kv head share few L2s) holding
+// its share of the total cost. With `blocks` > 0 the shares follow the workgroups b < blocks of
+// each group and every run holds at least one unit per workgroup; otherwise the shares are
+// equal. Runs of equal unit counts per XCD would not balance (with 4 kv heads on 8 XCDs, one XCD
+// of each pair would take the long tiles of its head and the other the short ones), and a run
+// that holds part of one kv head leaves an XCD units of one size, which its compute units
+// cannot share out evenly. So a group is as many XCDs as share one kv head's units (8 / kv
+// heads, rounded down to a power of two; one XCD at 8 or more kv heads), and it deals the long
+// and the short units of its run among them.
+int xcd_group_size(int32_t num_kv_heads) {
+  int xg = 1;
+  while (xg * 2 <= kXcds && xg * 2 * num_kv_heads <= kXcds) xg *= 2;
+  return xg;
+}
+std::vector<int64_t> group_runs(const PrefillItem* items, int32_t n, int32_t num_kv_heads, int32_t blocks, int xg) {
+  const int groups = kXcds / xg;
   const int64_t n_units = (int64_t)n * num_kv_heads;
   std::vector<int64_t> prefix((size_t)n_units + 1, 0);
   for (int64_t u = 0; u < n_units; ++u) prefix[(size_t)u + 1] = prefix[(size_t)u] + unit_cost(items[u % n]);
   auto blocks_of = [&](int g) {  // workgroups b < blocks with b % kXcds in group g
     int64_t c = 0;
-    for (int x = g * kXcdGroup; x < (g + 1) * kXcdGroup; ++x) c += blocks > x ? (blocks - 1 - x) / kXcds + 1 : 0;
+    for (int x = g * xg; x < (g + 1) * xg; ++x) c += blocks > x ? (blocks - 1 - x) / kXcds + 1 : 0;
     return c;
   };
-  std::vector<int64_t> run((size_t)kGroups + 1, 0);
-  const int64_t weight_total = blocks > 0 ? blocks : kGroups;
+  std::vector<int64_t> run((size_t)groups + 1, 0);
+  const int64_t weight_total = blocks > 0 ? blocks : groups;
   int64_t weight_before = 0, start = 0;
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < groups; ++g) {
     const int64_t bg = blocks > 0 ? blocks_of(g) : 0;
     weight_before += blocks > 0 ? bg : 1;
     const int64_t min_after = blocks > 0 ? blocks - weight_before : 0;
     int64_t e = n_units;
-    if (g < kGroups - 1) {
+    if (g < groups - 1) {
       // the first end whose prefix reaches the target, or the one before it if that is closer
       const int64_t target = (prefix[(size_t)n_units] * weight_before + weight_total / 2) / weight_total;
       e = std::lower_bound(prefix.begin() + start, prefix.end(), target) - prefix.begin();
@@ -104,14 +112,15 @@ std::vector<int64_t> group_runs(const PrefillItem* items, int32_t n, int32_t num
 // longest first, is dealt round-robin to its XCDs, so every XCD starts its longest units first
 // and its compute units fill in behind them with the short ones.
 std::vector<int32_t> block_table(const PrefillItem* items, int32_t n, int32_t num_kv_heads) {
-  const std::vector<int64_t> run = group_runs(items, n, num_kv_heads, 0);
+  const int xg = xcd_group_size(num_kv_heads);
+  const std::vector<int64_t> run = group_runs(items, n, num_kv_heads, 0, xg);
   std::vector<std::vector<int32_t>> per_xcd(kXcds);
-  for (int g = 0; g < kGroups; ++g) {
+  for (int g = 0; g < kXcds / xg; ++g) {
     std::vector<int64_t> order;
     for (int64_t u = run[(size_t)g]; u < run[(size_t)g + 1]; ++u) order.push_back(u);
     std::stable_sort(order.begin(), order.end(),
                      [&](int64_t a, int64_t b) { return unit_cost(items[a % n]) > unit_cost(items[b % n]); });
-    for (size_t r = 0; r < order.size(); ++r) per_xcd[(size_t)g * kXcdGroup + r % kXcdGroup].push_back((int32_t)order[r]);
+    for (size_t r = 0; r < order.size(); ++r) per_xcd[(size_t)(g * xg) + r % (size_t)xg].push_back((int32_t)order[r]);
   }
   size_t len = 0;
   for (const auto& l : per_xcd) len = std::max(len, l.size());
@@ -119,53 +128,6 @@ std::vector<int32_t> block_table(const PrefillItem* items, int32_t n, int32_t nu
   for (int x = 0; x < kXcds; ++x)
     for (size_t k = 0; k < per_xcd[(size_t)x].size(); ++k) table[k * kXcds + (size_t)x] = per_xcd[(size_t)x][k];
   return table;
-}
-
-// Lowers the largest chain load of a group left by the longest-first dealing: while a move of
-// one unit of the most loaded chain to another chain, or a swap with a shorter unit there,
-// lowers the larger of the two loads below the maximum, make the best such change (ties: the
-// first found). Bounded; deterministic.
-template <class Cost>
-void refine_chains(std::vector<std::vector<int64_t>>& chain, std::vector<int64_t>& load, const Cost& cost) {
-  const size_t nb = chain.size();
-  if (nb < 2) return;
-  for (size_t iter = 0; iter < 4 * nb; ++iter) {
-    size_t m = 0;
-    for (size_t j = 1; j < nb; ++j)
-      if (load[j] > load[m]) m = j;
-    const int64_t M = load[m];
-    int64_t best = M;
-    size_t bi = 0, bb = 0, bj = 0;
-    bool found = false, swap = false;
-    for (size_t i = 0; i < chain[m].size(); ++i) {
-      const int64_t cu = cost(chain[m][i]);
-      for (size_t b = 0; b < nb; ++b) {
-        if (b == m) continue;
-        const int64_t moved = std::max(load[b] + cu, M - cu);
-        if (moved < best) { best = moved; bi = i; bb = b; found = true; swap = false; }
-        for (size_t j = 0; j < chain[b].size(); ++j) {
-          const int64_t cv = cost(chain[b][j]);
-          if (cv >= cu) continue;
-          const int64_t swapped = std::max(M - cu + cv, load[b] - cv + cu);
-          if (swapped < best) { best = swapped; bi = i; bb = b; bj = j; found = true; swap = true; }
-        }
-      }
-    }
-    if (!found) return;
-    const int64_t u = chain[m][bi], cu = cost(u);
-    if (swap) {
-      const int64_t v = chain[bb][bj], cv = cost(v);
-      chain[m][bi] = v;
-      chain[bb][bj] = u;
-      load[m] += cv - cu;
-      load[bb] += cu - cv;
-    } else {
-      chain[m].erase(chain[m].begin() + (std::ptrdiff_t)bi);
-      chain[bb].push_back(u);
-      load[m] -= cu;
-      load[bb] += cu;
-    }
-  }
 }
 
 // Largest slot count n with align(n*D*4) + align(n*4) <= avail.
@@ -178,12 +140,13 @@ std::vector<UnitRecord> build_chains(const PrefillItem* items, int32_t n, int32_
   std::vector<UnitRecord> rec((size_t)n_units);
   int32_t next_free = nb;
   auto cost = [&](int64_t u) { return unit_cost(items[u % n]); };
-  const std::vector<int64_t> run_begin = group_runs(items, n, num_kv_heads, nb);
-  for (int g = 0; g < kGroups; ++g) {
+  const int xg = xcd_group_size(num_kv_heads);
+  const std::vector<int64_t> run_begin = group_runs(items, n, num_kv_heads, nb, xg);
+  for (int g = 0; g < kXcds / xg; ++g) {
     const int64_t u0 = run_begin[(size_t)g], len = run_begin[(size_t)g + 1] - u0;
     std::vector<int32_t> blocks;
     for (int32_t b = 0; b < nb; ++b)
-      if ((b % kXcds) / kXcdGroup == g) blocks.push_back(b);
+      if ((b % kXcds) / xg == g) blocks.push_back(b);
     if (len == 0) continue;
     std::vector<int64_t> order((size_t)len);
     for (int64_t k = 0; k < len; ++k) order[(size_t)k] = u0 + k;
@@ -197,9 +160,6 @@ std::vector<UnitRecord> build_chains(const PrefillItem* items, int32_t n, int32_
       load[k] += cost(u);
       chain[k].push_back(u);
     }
-    refine_chains(chain, load, cost);
-    for (auto& c : chain)  // longest first again (the refinement moves units between chains)
-      std::stable_sort(c.begin(), c.end(), [&](int64_t a, int64_t b) { return cost(a) > cost(b) || (cost(a) == cost(b) && a < b); });
     // A workgroup's finish time is the sum over its chain, whatever the order; rotating the
     // j-th workgroup's chain (of its group) by j keeps neighbours from switching units (a
     // burst of Q reads and O writes) at the same moments.

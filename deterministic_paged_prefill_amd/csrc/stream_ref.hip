@@ -5,10 +5,13 @@
 // compared against.
 //
 // Grid: `split` workgroups of 512 threads per unit (item, kv head) of the plan, work index
-// w = xcd_chunked(b, split * units) as in the attention launch; workgroup w covers the keys
-// [lo + part * len / split, lo + (part + 1) * len / split) of its unit, part = w % split.
-// Each 64-lane load moves 1 KiB: 16-byte chunks of consecutive key rows of one tensor. A wave
-// keeps DEPTH loads in flight (counted waits), into a ring of 16 one-KiB LDS slots per wave.
+// w = xcd_chunked(b, split * units) as in the attention launch, part = w % split. By keys:
+// workgroup w covers the keys [lo + part * len / split, lo + (part + 1) * len / split) of its
+// unit. By head_dim halves (split 2, DPP_STREAM_HEAD_SPLIT): workgroup w reads all of its
+// unit's K and the part-th half of every V row, the gather of the head_dim-split attention
+// launch. Each 64-lane load moves 1 KiB: 16-byte chunks of consecutive key rows (or half rows)
+// of one tensor. A wave keeps DEPTH loads in flight (counted waits), into a ring of 16 one-KiB
+// LDS slots per wave.
 #include <hip/hip_runtime.h>
 
 #include <string>
@@ -51,6 +54,7 @@ struct StreamArgs {
   int32_t page_size;
   int32_t row_bytes;   // one key row of one kv head: head_dim x element size
   int32_t block_n;
+  int32_t head_split;  // 1: split 2 by head_dim halves of V (all of K in both)
   uint32_t plan_id;
 };
 
@@ -67,13 +71,19 @@ __global__ __launch_bounds__(kStreamThreads, 1) void stream_kernel(StreamArgs a)
   const int key_lo = it.kv_tile_begin * a.block_n;
   const int key_hi = min(it.kv_tile_end * a.block_n, it.req.kv_len);
   const int len = max(key_hi - key_lo, 0);
-  const int k0 = key_lo + (int)((int64_t)len * part / a.split);
-  const int k1 = key_lo + (int)((int64_t)len * (part + 1) / a.split);
+  const int k0 = a.head_split ? key_lo : key_lo + (int)((int64_t)len * part / a.split);
+  const int k1 = a.head_split ? key_lo + len : key_lo + (int)((int64_t)len * (part + 1) / a.split);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int chunks_per_row = a.row_bytes / 16;
   const int rows_per_load = 64 / chunks_per_row;
+  // V: whole rows, or (head split) the part-th half of each row
+  const int v_bytes = a.head_split ? a.row_bytes / 2 : a.row_bytes;
+  const int v_chunks = v_bytes / 16;
+  const int v_rows_per_load = 64 / v_chunks;
   const int64_t token_bytes = (int64_t)a.num_kv_heads * a.row_bytes;
-  const int n_loads = 2 * ((k1 - k0 + rows_per_load - 1) / rows_per_load);  // K and V
+  const int n_k = (k1 - k0 + rows_per_load - 1) / rows_per_load;
+  const int n_v = (k1 - k0 + v_rows_per_load - 1) / v_rows_per_load;
+  const int n_loads = n_k + n_v;  // K and V loads alternate while both remain
   const uint32_t ring = (uint32_t)(uintptr_t)smem + (uint32_t)wave * kSlots * 1024u;
   // this workgroup's page ids into LDS first: a page-id load inside the stream would make the
   // compiler wait for every DMA load in flight
@@ -83,10 +93,12 @@ __global__ __launch_bounds__(kStreamThreads, 1) void stream_kernel(StreamArgs a)
   for (int j = threadIdx.x; j < n_pg; j += kStreamThreads) table[j] = a.kv_indices[it.req.page_start + pg0 + j];
   __syncthreads();
   int issued = 0;
+  const int both = 2 * min(n_k, n_v);
   for (int i = wave; i < n_loads; i += kStreamThreads / 64) {
-    const bool v = i & 1;
-    const int key = k0 + (i >> 1) * rows_per_load + lane / chunks_per_row;
-    const int col = (lane % chunks_per_row) * 16;
+    const bool v = i < both ? (i & 1) : n_v > n_k;
+    const int j = i < both ? i >> 1 : i - both + both / 2;  // index among this tensor's loads
+    const int key = v ? k0 + j * v_rows_per_load + lane / v_chunks : k0 + j * rows_per_load + lane / chunks_per_row;
+    const int col = v ? (a.head_split ? part * v_bytes : 0) + (lane % v_chunks) * 16 : (lane % chunks_per_row) * 16;
     const unsigned char* src = reinterpret_cast<const unsigned char*>(pre->zero_chunk);
     if (key < k1) {
       const int pi = key / a.page_size;
@@ -129,6 +141,8 @@ extern "C" dpp_status dpp_stream_kv(const dpp_plan* plan, const void* k_pool, co
   if (!plan) return fail(DPP_ERR_INVALID, "dpp_stream_kv: null plan");
   if (plan->ragged) return fail(DPP_ERR_UNSUPPORTED, "dpp_stream_kv: paged plans only");
   if (split < 1 || split > 8) return fail(DPP_ERR_INVALID, "dpp_stream_kv: split must be in [1, 8]");
+  const bool head_split = (flags & DPP_STREAM_HEAD_SPLIT) != 0;
+  if (head_split && split != 2) return fail(DPP_ERR_INVALID, "dpp_stream_kv: DPP_STREAM_HEAD_SPLIT needs split 2");
   if (depth != 4 && depth != 8 && depth != 16 && depth != 32)
     return fail(DPP_ERR_INVALID, "dpp_stream_kv: depth must be 4, 8, 16 or 32");
   if (num_pages < 0 || plan->total_kv_entries > num_kv_indices)
@@ -139,7 +153,10 @@ extern "C" dpp_status dpp_stream_kv(const dpp_plan* plan, const void* k_pool, co
   const int row_bytes = plan->cfg.head_dim * (plan->cfg.kv_dtype == DPP_KV_FP8_E4M3 ? 1 : 2);
   if (row_bytes % 16 != 0 || 64 % (row_bytes / 16) != 0)
     return fail(DPP_ERR_UNSUPPORTED, "dpp_stream_kv: key rows must split 1 KiB loads evenly");
-  if (flags & ~DPP_RUN_REUSE_UPLOAD) return fail(DPP_ERR_INVALID, "dpp_stream_kv: unknown flags");
+  if (head_split && (row_bytes % 32 != 0 || 64 % (row_bytes / 32) != 0))
+    return fail(DPP_ERR_UNSUPPORTED, "dpp_stream_kv: half rows must split 1 KiB loads evenly");
+  if (flags & ~(DPP_RUN_REUSE_UPLOAD | DPP_STREAM_HEAD_SPLIT))
+    return fail(DPP_ERR_INVALID, "dpp_stream_kv: unknown flags");
   if (plan->num_items == 0) return DPP_OK;
   if (!(flags & DPP_RUN_REUSE_UPLOAD)) {
     // the plan's work list must be in the workspace (upload it here, on this stream)
@@ -161,6 +178,7 @@ extern "C" dpp_status dpp_stream_kv(const dpp_plan* plan, const void* k_pool, co
   a.page_size = plan->cfg.page_size;
   a.row_bytes = row_bytes;
   a.block_n = plan->block_n;
+  a.head_split = head_split ? 1 : 0;
   a.plan_id = plan->plan_id;
   hipError_t e;
   switch (depth) {

@@ -257,11 +257,15 @@ dpp_status dpp_run_static(const dpp_plan* plan, const void* q, int64_t q_rows, c
  * Read-only streaming reference of a plan's KV gather (a measurement tool, not part of the
  * attention): every K and V byte the plan's prefill units read, each once, is moved into LDS
  * by LDS-DMA and dropped, by `split` workgroups per unit (item, kv head) with `depth` (4, 8, 16
- * or 32) 1 KiB loads in flight per wave. Its time is the ceiling the memory-bound launches of
- * the same plan (short extends, long-KV decodes) are measured against. Arguments as dpp_run;
- * paged plans only; flags 0 or DPP_RUN_REUSE_UPLOAD (the workspace already holds this plan's
- * work list). Writes only the workspace head.
+ * or 32) 1 KiB loads in flight per wave. The workgroups of a unit divide its keys; with
+ * DPP_STREAM_HEAD_SPLIT (split 2 only) both read all of its K and each one half of every V row,
+ * as the head_dim-split attention launch does. Its time is the ceiling the memory-bound
+ * launches of the same plan (short extends, long-KV decodes) are measured against. Arguments as
+ * dpp_run; paged plans only; flags: DPP_RUN_REUSE_UPLOAD (the workspace already holds this
+ * plan's work list) and DPP_STREAM_HEAD_SPLIT. Writes only the workspace head.
  */
+#define DPP_STREAM_HEAD_SPLIT 2u
+
 dpp_status dpp_stream_kv(const dpp_plan* plan, const void* k_pool, const void* v_pool,
                          int64_t num_pages, const int32_t* kv_indices, int64_t num_kv_indices,
                          void* workspace, size_t workspace_bytes, int32_t split, int32_t depth,

@@ -74,3 +74,36 @@ def test_side_stream_without_workspace(work):
     for i, (o, l) in enumerate(outs):
         assert_bits_equal(o.cpu(), o_ref.cpu(), f"side-stream run {i} o")
         assert_bits_equal(l.cpu(), l_ref.cpu(), f"side-stream run {i} lse")
+
+
+def test_stream_reference_runs_every_mode():
+    """The read-only streaming reference (a measurement tool) runs by keys (1, 2 and 4
+    workgroups per unit) and by head_dim halves, at every load depth, over a narrow extend plan
+    with the head_dim-split launch's grid and a wide prefill plan, and leaves the workspace
+    beyond the work list untouched."""
+    import deterministic_paged_prefill_amd as dpp
+    ext = wl.extend_batch(layout="distinct")
+    long = wl.random_workload(97, hq=32, hkv=8, d=128, page_size=16, kv_dtype="bf16", specs=[(9000, 900)])
+    lib = dpp.library()
+    for work, name in ((ext, "cached"), (ext, "full"), (long, "batch")):
+        dev = Device(work)
+        b = work.batches[name]
+        p = dev.plan(b)
+        assert name != "batch" or p.info.workspace_bytes > p.info.header_bytes, "a plan with partials"
+        kvi = torch.from_numpy(b.kv_indices).cuda()
+        ws = p.new_workspace()
+        ws.fill_(0x5A)
+        p.upload(ws)
+        head = p.info.header_bytes
+        torch.cuda.synchronize()
+        stream = torch.cuda.current_stream().cuda_stream
+        for split, flags in ((1, 0), (2, 0), (4, 0), (2, dpp.STREAM_HEAD_SPLIT)):
+            for depth in (4, 8, 16, 32):
+                say(f"stream reference {name}: split {split} flags {flags} depth {depth}")
+                st = lib.dpp_stream_kv(p._h, dev.k_pool.data_ptr(), dev.v_pool.data_ptr(), dev.k_pool.shape[0],
+                                       kvi.data_ptr(), kvi.numel(), ws.data_ptr(), ws.numel(), split, depth,
+                                       dpp.RUN_REUSE_UPLOAD | flags, stream)
+                assert st == 0, lib.dpp_last_error()
+        torch.cuda.synchronize()
+        rest = ws[head:].cpu().numpy()
+        assert (rest == 0x5A).all(), "the reference writes nothing past the work list"

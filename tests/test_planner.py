@@ -170,11 +170,17 @@ def test_cap_bounds_workspace_and_adds_passes(dpp, cap_mib):
     assert sorted(map(key, parse(p.header()).items)) == sorted(map(key, parse(unbounded.header()).items))
 
 
-XCD_GROUP = 2  # neighbouring XCDs that share one run of the plain launch order
+def _xcd_group(hkv, xcds=8):
+    """Neighbouring XCDs that share one run of the plain launch order: as many as share one kv
+    head's units (8 / kv heads rounded down to a power of two, at least 1)."""
+    xg = 1
+    while xg * 2 <= xcds and xg * 2 * hkv <= xcds:
+        xg *= 2
+    return xg
 
 
-def _group_of(b, xcds=8):
-    return (b % xcds) // XCD_GROUP
+def _group_of(b, hkv, xcds=8):
+    return (b % xcds) // _xcd_group(hkv, xcds)
 
 
 def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
@@ -200,7 +206,7 @@ def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
             i = index[tuple(int(x) for x in rec[:3])]
             assert (rec[:7] == items[i][:7]).all() and (rec[8:12] == items[i][8:12]).all()
             h = int(rec[12])
-            group_units.setdefault(_group_of(b, xcds), []).append(h * n + i)  # plain launch order
+            group_units.setdefault(_group_of(b, hkv, xcds), []).append(h * n + i)  # plain launch order
             covered.add((i, h))
             c = cost(rec)
             costs.append(c)
@@ -212,8 +218,8 @@ def _check_chains(parsed, items, units, hkv, blocks=256, xcds=8):
     assert seen.all(), "every record is on a chain"
     assert covered == {(i, h) for i in range(n) for h in range(hkv)}
     biggest = max(cost(u) for u in units)
-    groups = xcds // XCD_GROUP
-    members = {g: [b for b in range(nb) if _group_of(b, xcds) == g] for g in range(groups)}
+    groups = xcds // _xcd_group(hkv, xcds)
+    members = {g: [b for b in range(nb) if _group_of(b, hkv, xcds) == g] for g in range(groups)}
     for g in range(groups):
         loads = [load[b] for b in members[g]]
         if loads:
@@ -244,15 +250,16 @@ def _check_table(table, items, hkv, xcds=8):
     used = t[t >= 0]
     assert sorted(used.tolist()) == list(range(n_units)), "every unit once"
     cost = np.array([int(items[u % n][5] - items[u % n][4]) + 2 for u in range(n_units)])
-    groups = xcds // XCD_GROUP
+    xg = _xcd_group(hkv, xcds)
+    groups = xcds // xg
     start = 0
     per_xcd = np.zeros(xcds)
     for g in range(groups):
-        blocks = [b for b in range(len(t)) if _group_of(b, xcds) == g and t[b] >= 0]
+        blocks = [b for b in range(len(t)) if _group_of(b, hkv, xcds) == g and t[b] >= 0]
         run = sorted(int(t[b]) for b in blocks)
         assert run == list(range(start, start + len(run))), "contiguous runs in group order"
         start += len(run)
-        for x in range(g * XCD_GROUP, (g + 1) * XCD_GROUP):
+        for x in range(g * xg, (g + 1) * xg):
             mine = [int(t[b]) for b in range(x, len(t), xcds)]
             live = [w for w in mine if w >= 0]
             assert mine[:len(live)] == live, "an XCD's blocks without a unit come last"
@@ -465,6 +472,29 @@ def test_run_rejects_bad_shapes_before_any_launch(dpp):
     assert st == dpp.DPP_ERR_INVALID
     st = lib.dpp_merge_states(fake, fake, 1, 2, 1, 130, fake, fake, None)
     assert st == dpp.DPP_ERR_UNSUPPORTED
+
+
+def test_stream_reference_rejects_bad_arguments(dpp):
+    """dpp_stream_kv's checks happen on the host before any HIP call (no GPU needed)."""
+    lib = dpp.library()
+    b = _specs_batch([(1028, 3)])
+    p = _plan(dpp, b)
+    fake = 1 << 20
+    ws = p.workspace_bytes
+    n = int(b.kv_indptr[-1])
+
+    def call(split=2, depth=4, flags=1, workspace=fake, kv=n):
+        return lib.dpp_stream_kv(p._h, fake, fake, 4096, fake, kv, workspace, ws, split, depth, flags, None)
+
+    assert call(split=0) == dpp.DPP_ERR_INVALID and b"split" in lib.dpp_last_error()
+    assert call(split=9) == dpp.DPP_ERR_INVALID
+    assert call(depth=5) == dpp.DPP_ERR_INVALID and b"depth" in lib.dpp_last_error()
+    assert call(split=1, flags=1 | dpp.STREAM_HEAD_SPLIT) == dpp.DPP_ERR_INVALID
+    assert b"split 2" in lib.dpp_last_error()
+    assert call(flags=4) == dpp.DPP_ERR_INVALID and b"unknown flags" in lib.dpp_last_error()
+    assert call(kv=n - 1) == dpp.DPP_ERR_SHAPE
+    assert call(workspace=fake + 16) == dpp.DPP_ERR_WORKSPACE
+    assert call(workspace=None) == dpp.DPP_ERR_INVALID
 
 
 def test_null_arguments(dpp):
