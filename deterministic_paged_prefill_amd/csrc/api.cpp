@@ -10,6 +10,7 @@
 #include <cstddef>
 #include <cstring>
 #include <map>
+#include <cmath>
 #include <string>
 
 #include "kernels.h"
@@ -162,6 +163,12 @@ dpp_status launch_passes(const dpp_plan* plan, const void* q, const void* k_pool
   a.scale_log2 = plan->scale_log2;
   a.k_scale = plan->cfg.k_scale;
   a.v_scale = plan->cfg.v_scale;
+  auto pow2_in_range = [](float x) {
+    int e = 0;
+    const float m = std::frexp(x, &e);  // x = m 2^e, m in [0.5, 1)
+    return m == 0.5f && e - 1 >= -64 && e - 1 <= 64;
+  };
+  a.kv_scale_pow2 = pow2_in_range(a.k_scale) && pow2_in_range(a.v_scale) ? 1 : 0;
 
   MergeArgs m{};
   m.header = a.header;

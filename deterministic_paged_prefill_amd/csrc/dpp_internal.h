@@ -198,6 +198,7 @@ struct PrefillArgs {
   float scale_log2;         // sm_scale * log2(e), rounded once to fp32
   float k_scale;
   float v_scale;
+  int32_t kv_scale_pow2;    // fp8: both scales are powers of two in [2^-64, 2^64]
 };
 
 struct MergeArgs {

@@ -145,6 +145,20 @@ __device__ inline u32x4 dequant8(u32x2 raw, float scale) {
   return out;
 }
 
+// The same for a power-of-two scale in [2^-64, 2^64]: v_cvt_scalef32_pk_bf16_fp8 decodes two
+// codes and applies the scale's exponent in one instruction. Every product is then an exact
+// normal bf16 (an E4M3 value has 4 significant bits, exponents -9..8), so the bits equal
+// dequant8's (checked on the GPU for all 256 codes at several scales).
+__device__ inline u32x4 dequant8_pow2(u32x2 raw, float scale) {
+  u32x4 out;
+#pragma unroll
+  for (int w = 0; w < 2; ++w) {
+    out[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[w], scale, false));
+    out[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(raw[w], scale, true));
+  }
+  return out;
+}
+
 __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -603,8 +617,10 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     unsigned char* vb = smem + vbuf_off(tv);
 #pragma unroll
     for (int i = 0; i < C::NCH; ++i) {
-      *reinterpret_cast<u32x4*>(kb + lds_k[i]) = dequant8(kreg[i], a.k_scale);
-      *reinterpret_cast<u32x4*>(vb + lds_v[i]) = dequant8(vreg[i], a.v_scale);
+      *reinterpret_cast<u32x4*>(kb + lds_k[i]) =
+          a.kv_scale_pow2 ? dequant8_pow2(kreg[i], a.k_scale) : dequant8(kreg[i], a.k_scale);
+      *reinterpret_cast<u32x4*>(vb + lds_v[i]) =
+          a.kv_scale_pow2 ? dequant8_pow2(vreg[i], a.v_scale) : dequant8(vreg[i], a.v_scale);
     }
   };
   auto issue_group = [&](int t) {  // bf16: DMA of load group t

@@ -44,13 +44,18 @@ def test_merge_states_against_oracle(oracle, R, S, H, D):
     assert np.abs(lg[fin] - lse_ref[fin]).max() <= 2e-5 * max(1.0, np.abs(lse_ref[fin]).max())
 
 
-def test_e4m3_decode_every_code(oracle):
+@pytest.mark.parametrize("v_scale", [None, 2.0 ** -60, 3.0])
+def test_e4m3_decode_every_code(oracle, v_scale):
     """Single-key rows return their value row exactly: o = bf16(decode(code) * v_scale).
 
-    Two 128-wide value rows hold all 256 codes; keys hold small finite codes."""
+    Two 128-wide value rows hold all 256 codes; keys hold small finite codes. Scales: the
+    workload's (a power of two: the kernels decode with the scaled conversion instruction), a
+    power of two near the end of that instruction's range, and 3 (the multiply path)."""
     hq, hkv, d, page = 1, 1, 128, 16
     work = wl.random_workload(77, hq=hq, hkv=hkv, d=d, page_size=page, kv_dtype="fp8_e4m3",
                               specs=[(1, 1), (1, 1)])
+    if v_scale is not None:
+        work.v_scale = v_scale
     b = work.batches["batch"]
     codes = torch.arange(256, dtype=torch.int32).to(torch.uint8).reshape(2, 128)
     for r, req in enumerate(b.requests):
