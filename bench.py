@@ -473,7 +473,10 @@ def main() -> int:
         def timed_leg(work, batch, steps, warmup):
             rr = Runner(work, batch, replicas=1)
             o, l = rr.outputs(0)
-            ms, _ = rr.timed(steps, warmup)
+            # matrix-heavy launches reach their steady clock after ~25 ms of work: warm up for
+            # at least 30 ms (one step timed first to size it)
+            one, _ = rr.timed(1, 0)
+            ms, _ = rr.timed(steps, max(warmup, int(30.0 / max(one, 1e-3)) + 1))
             info = rr.plan.info
             del rr
             return ms, o, l, info
