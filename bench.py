@@ -376,6 +376,9 @@ def main() -> int:
             ms, wall = run.timed(args.steps, args.warmup)
             log(f"extend: {ms * 1e3:.2f} us/step (wall {wall * 1e3:.2f} us)")
             return 0
+        # timed before the host-side checks below, whose CPU thread pool would otherwise still
+        # be spinning while the launches are issued
+        ms, wall = run.timed(args.steps, args.warmup)
         # the metric's bit-exactness clause: cached rows vs the same rows of a full prefill
         o_c, l_c = run.outputs(0)
         fr = Runner(work, full, replicas=1)
@@ -388,7 +391,6 @@ def main() -> int:
         assert np.isfinite(o_c.float().numpy()).all()
         del fr
         log(f"cached-vs-full max|diff| = {max_diff}")
-        ms, wall = run.timed(args.steps, args.warmup)
         ms_graph = run.graph_timed(40, 10)
         ceiling = run.stream_ceiling(args.steps, args.warmup, same_gather=True)
         replan = run.replan_us()
