@@ -628,47 +628,47 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     dma_tile(true, t + VA);
   };
   // Scalar pages. Load i of this wave in tile t covers key rows [key0, key0 + KPI) of one
-  // page; its page id is read from the LDS table one iteration ahead (a uniform read that
-  // queues behind the iteration's other LDS traffic) and moved to a scalar register.
+  // page, so its address is uniform: a buffer descriptor in scalar registers. The kLoads
+  // descriptors of a group are computed side by side, load j in lane j (vector arithmetic,
+  // a few instructions for all of them), then moved to scalar registers with readlane; lane j
+  // reads its page id from the LDS table one iteration ahead.
   auto page_slot = [&](int t, int i) {
     const int kt = kt0 + min(max(t, 0), n_tiles - 1);
     const int key0 = kt * C::BN + (i * IW + iw) * C::KPI;
     return min((key0 >> page_shift) - key_lo_page, n_pages - 1);
   };
-  int32_t ids[2][NCHT];  // page ids of the next group's K and V loads (uniform values)
-  auto read_ids = [&](int g) {
-#pragma unroll
-    for (int i = 0; i < NCHT; ++i) {
-      ids[0][i] = pg_lds[page_slot(g + KA, i)];
-      ids[1][i] = pg_lds[page_slot(g + VA, i)];
-    }
-  };
+  constexpr int kLoads = 2 * NCHT;
+  const int lj = min(lane, kLoads - 1);  // the load this lane prepares (lanes past kLoads: a copy)
+  const bool lj_v = lj >= NCHT;          // a V load
+  const int lj_i = lj_v ? lj - NCHT : lj;
+  int32_t lane_id = 0;  // page id of this lane's load of the next group
+  auto read_ids = [&](int g) { lane_id = pg_lds[page_slot(lj_v ? g + VA : g + KA, lj_i)]; };
   // Descriptors of the next group's loads, prepared ahead so that firing a load is an M0
   // write and the load itself.
   struct LoadDesc {
     i32x4 rsrc;
     uint32_t lds;
   };
-  constexpr int kLoads = 2 * NCHT;
   LoadDesc nd[kLoads];
-  auto prep = [&](int grp) {  // from ids (group grp's page ids)
+  auto prep = [&](int grp) {  // from lane_id (group grp's page ids)
+    const int t = lj_v ? grp + VA : grp + KA;
+    const int id = lane_id;
+    const bool good = id >= 0 && id < a.num_pages;  // else the load reads zeros
+    const uint64_t base = reinterpret_cast<uint64_t>(lj_v ? vbase : kbase);
+    const bool tile_ok = t >= 0 && t < n_tiles;
+    const int key0 = (kt0 + min(max(t, 0), n_tiles - 1)) * C::BN + (lj_i * IW + iw) * C::KPI;
+    const uint64_t off = good ? (uint64_t)(uint32_t)id * (uint64_t)page_bytes : 0;
+    const int rows = min(max(rq.kv_len - key0, 0), C::KPI);
+    const uint32_t bytes = (tile_ok && good) ? (uint32_t)rows * (uint32_t)token_bytes : 0u;
+    const uint64_t addr = base + off + (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
+    const uint32_t lds =
+        lds0 + (uint32_t)(((lj_v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES + (lj_i * IW + iw) * 1024);
 #pragma unroll
     for (int j = 0; j < kLoads; ++j) {
-      const bool v = j >= NCHT;
-      const int i = v ? j - NCHT : j;
-      const int t = v ? grp + VA : grp + KA;
-      const int id = __builtin_amdgcn_readfirstlane(ids[v ? 1 : 0][i]);
-      const bool good = id >= 0 && id < a.num_pages;  // else the load reads zeros
-      const uint64_t base = reinterpret_cast<uint64_t>(v ? vbase : kbase);
-      const bool tile_ok = t >= 0 && t < n_tiles;
-      const int key0 = (kt0 + min(max(t, 0), n_tiles - 1)) * C::BN + (i * IW + iw) * C::KPI;
-      const uint64_t off = good ? (uint64_t)(uint32_t)id * (uint64_t)page_bytes : 0;
-      const int rows = min(max(rq.kv_len - key0, 0), C::KPI);
-      const uint32_t bytes = (uint32_t)__builtin_amdgcn_readfirstlane(
-          (int)((tile_ok && good) ? (uint32_t)rows * (uint32_t)token_bytes : 0u));
-      const uint64_t addr = base + off + (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
-      nd[j].rsrc = buffer_rsrc(uniform64(addr), bytes);
-      nd[j].lds = lds0 + (uint32_t)(((v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES + (i * IW + iw) * 1024);
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)addr, j);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), j);
+      nd[j].rsrc = buffer_rsrc(((uint64_t)hi << 32) | lo, (uint32_t)__builtin_amdgcn_readlane((int)bytes, j));
+      nd[j].lds = (uint32_t)__builtin_amdgcn_readlane((int)lds, j);
     }
   };
   auto fire = [&](int j) { dma16_buf(j < NCHT ? voff_k[j] : voff_v[j - NCHT], nd[j].rsrc, nd[j].lds); };
