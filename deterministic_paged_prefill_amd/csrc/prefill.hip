@@ -354,7 +354,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   int kvh, cur_next;
   PrefillItem it;
   RequestDesc rq;
-  int tile_rows, ctx, split_key0, p_min, kt0, n_tiles, key_lo_page, n_pages;
+  int tile_rows, ctx, p_min, kt0, n_tiles, key_lo_page, n_pages;
   bool has_rows, s_rows, o_rows;
   int p_row[NB];  // position of the lane's rows (INT_MAX past the tile: no key is masked)
   const unsigned char* kbase;  // the unit's kv head inside the K and V pools
@@ -379,7 +379,6 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     rq = u.req;
     tile_rows = min(C::PLAN_BM, rq.qo_len * g - it.row_start);
     ctx = rq.kv_len - rq.qo_len;  // position of query token 0
-    split_key0 = it.split * kSplitTokens;
     has_rows = row_wave * C::RPW < tile_rows;  // wave-uniform
     s_rows = has_rows && (!kSpec || wave == 0);  // scores and softmax
     o_rows = has_rows && (!kSpec || wave == 4);  // output
