@@ -472,7 +472,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   //         swizzled slot.
   //   fp8:  chunk q = tid + THREADS i, loaded to registers, decoded, stored to its slot.
   constexpr bool pow2_pages = MODE != kPagesGeneral;
-  static_assert(!(FP8 && MODE == kPagesScalar), "fp8 stages through registers");
+  // (fp8 with scalar pages: register loads through buffer descriptors, see fp8_load)
   // Waves that issue DMA loads: 2, 3, 6, 7 in the narrow bf16 kernel, otherwise all.
   constexpr int IW = kSpec ? 4 : C::WAVES;
   const int iw = kSpec ? ((wave & 1) | ((wave >> 2) << 1)) : wave;  // index among the issuers
@@ -604,11 +604,55 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
   };
   u32x2 kreg[C::NCH], vreg[C::NCH];  // fp8 staging of one load group
-  auto fp8_load = [&](int tk, int tv) {
+  // fp8 with scalar pages (a power-of-two page size holding the K8 = 64 / CH key rows of one
+  // wave's load): load i of this wave covers rows [r0(i), r0(i) + K8) of its tile, one page,
+  // so it reads through a buffer descriptor (uniform) at a per-lane offset; keys past kv_len
+  // and pages outside the pool read zeros by the descriptor's range. The 2 NCH descriptors of
+  // a group are computed one per lane (lane j: load j, K for j < NCH) and moved to scalar
+  // registers with readlane; lane j reads its page id from the LDS table one group ahead.
+  constexpr int K8 = 64 / C::CH;
+  constexpr int kLoads8 = 2 * C::NCH;
+  const int l8 = min(lane, kLoads8 - 1);
+  const bool l8_v = l8 >= C::NCH;
+  const int l8_r0 = ((64 * wave + C::THREADS * (l8_v ? l8 - C::NCH : l8)) / C::CH);  // r0 of the lane's load
+  const int voff8 = (lane / C::CH) * (int)token_bytes + (lane % C::CH) * 8;
+  int32_t id8 = 0;  // page id of this lane's load of the next group
+  auto read_ids8 = [&](int tk, int tv) {
+    const int kt = kt0 + min(max(l8_v ? tv : tk, 0), n_tiles - 1);
+    id8 = pg_lds[min(((kt * C::BN + l8_r0) >> page_shift) - key_lo_page, n_pages - 1)];
+  };
+  auto fp8_load_scalar = [&](int tk, int tv) {
+    const int t = l8_v ? tv : tk;
+    const bool good = id8 >= 0 && id8 < a.num_pages;
+    const bool tile_ok = t >= 0 && t < n_tiles;
+    const int key0 = (kt0 + min(max(t, 0), n_tiles - 1)) * C::BN + l8_r0;
+    const int rows = min(max(rq.kv_len - key0, 0), K8);
+    const uint32_t bytes = (tile_ok && good) ? (uint32_t)rows * (uint32_t)token_bytes : 0u;
+    const uint64_t addr = reinterpret_cast<uint64_t>(l8_v ? vbase : kbase) +
+                          (good ? (uint64_t)(uint32_t)id8 * (uint64_t)page_bytes : 0) +
+                          (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
 #pragma unroll
-    for (int i = 0; i < C::NCH; ++i) {
-      kreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(kbase, kcol[i], krow[i], tk));
-      vreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(vbase, vcol[i], krow[i], tv));
+    for (int j = 0; j < kLoads8; ++j) {
+      const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)addr, j);
+      const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(addr >> 32), j);
+      const int nrec = __builtin_amdgcn_readlane((int)bytes, j);
+      const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(((uint64_t)hi << 32) | lo), (short)0, nrec, 0x00020000);
+      const u32x2 val = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff8, 0, 0));
+      if (j < C::NCH) kreg[j] = val;
+      else vreg[j - C::NCH] = val;
+    }
+    read_ids8(tk + 1, tv + 1);
+  };
+  auto fp8_load = [&](int tk, int tv) {
+    if constexpr (FP8 && MODE == kPagesScalar) {
+      fp8_load_scalar(tk, tv);
+    } else {
+#pragma unroll
+      for (int i = 0; i < C::NCH; ++i) {
+        kreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(kbase, kcol[i], krow[i], tk));
+        vreg[i] = *reinterpret_cast<const u32x2*>(chunk_src(vbase, vcol[i], krow[i], tv));
+      }
     }
   };
   auto fp8_store = [&](int tk, int tv) {
@@ -1016,6 +1060,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
   } else if constexpr (!kPP) {
     if constexpr (FP8) {
+      if constexpr (MODE == kPagesScalar) read_ids8(0, -2);  // the first group's page ids
 #pragma unroll
       for (int t = -C::NBUF; t < -1; ++t) {
         fp8_load(t + C::NBUF, t + C::NBUF - 2);
@@ -1251,6 +1296,8 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   const bool pow2 = (P & (P - 1)) == 0;
   if constexpr (BNX == block_n_for(D)) {
     if (fp8) {  // one fp8 schedule: NARROW changes nothing in it
+      constexpr int kRowsPerLoad8 = 64 / (D / 8);  // key rows of one wave's fp8 load
+      if (pow2 && P >= kRowsPerLoad8) return launch_one<D, true, NB, false, kPagesScalar>(a, stream);
       return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, false, kPagesPow2>(a, stream)
                                          : launch_one<D, true, NB, false, kPagesGeneral>(a, stream);
     }
