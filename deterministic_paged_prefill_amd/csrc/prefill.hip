@@ -241,11 +241,14 @@ __device__ inline void wait_vmcnt() {
 //   kPagesGeneral  any page size: per-lane division by page_size
 //   kPagesPow2     page_size a power of two no larger than a KV tile: a chunk's page within
 //                  its tile and its offset in that page are the same for every tile
-//   kPagesScalar   bf16, page_size a power of two holding whole DMA loads (a multiple of the
+//   kPagesScalar   page_size a power of two holding whole wave-wide loads (a multiple of the
 //                  keys one load covers): the page of a load is uniform, its address is built
-//                  in scalar registers as a buffer descriptor whose size ends at kv_len (the
-//                  hardware returns zeros past it)
-constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2;
+//                  as a buffer descriptor in scalar registers whose size ends at kv_len (the
+//                  hardware returns zeros past it); bf16 loads are LDS-DMA, fp8 loads go to
+//                  registers
+//   kPagesScalarDiv the same for any other page size holding whole loads (page and row of a
+//                  key by division)
+constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2, kPagesScalarDiv = 3;
 
 // NB: 16-row blocks per wave. VH (narrow bf16 kernel only): the launch runs every unit on two
 // workgroups, one per half of head_dim in PV. Both compute the unit's scores and softmax from
@@ -261,7 +264,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   // same SIMD) the output, and waves 2, 3, 6, 7 issue the DMA loads.
   static_assert(!NARROW || NB == 1, "a narrow tile is one 16-row block");
   constexpr bool kSpec = !FP8 && NARROW && waves_for(D) == 8;
-  static_assert(!VH || (kSpec && MODE != kPagesScalar), "head_dim halves: narrow bf16 kernel, vector addresses");
+  constexpr bool kScalar = MODE == kPagesScalar || MODE == kPagesScalarDiv;  // buffer descriptors
+  static_assert(!VH || (kSpec && !kScalar), "head_dim halves: narrow bf16 kernel, vector addresses");
   // V ring: rows of head_dim (or of half of it, VH) per tile
   constexpr int VROW = VH ? C::ROW_BYTES / 2 : C::ROW_BYTES;
   constexpr int VTILE = VH ? C::TILE_BYTES / 2 : C::TILE_BYTES;
@@ -347,6 +351,15 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int row_wave = kSpec ? 0 : wave;  // whose 16-row blocks this wave works on
   const int page_size = a.page_size;
   const int page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz(page_size) : -1;
+  // page of a key and the key's row in it (scalar page modes)
+  auto page_of = [&](int key) {
+    if constexpr (MODE == kPagesScalarDiv) return key / page_size;
+    else return key >> page_shift;
+  };
+  auto row_in_page = [&](int key) {
+    if constexpr (MODE == kPagesScalarDiv) return key % page_size;
+    else return key & (page_size - 1);
+  };
   const int64_t token_bytes = (int64_t)a.num_kv_heads * D * kElem;
   const int64_t page_bytes = token_bytes * page_size;
 
@@ -595,7 +608,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
   };
   auto dma_tile = [&](bool v, int t) {
-    if constexpr (MODE == kPagesScalar) {
+    if constexpr (kScalar) {
       // scalar pages are issued by issue_group_scalar
     } else if (v) {
       dma_chunks(vbase, lds0 + (uint32_t)vbuf_off(t), t, vrow, vpg_rel, vin_page, vcolh);
@@ -619,7 +632,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   int32_t id8 = 0;  // page id of this lane's load of the next group
   auto read_ids8 = [&](int tk, int tv) {
     const int kt = kt0 + min(max(l8_v ? tv : tk, 0), n_tiles - 1);
-    id8 = pg_lds[min(((kt * C::BN + l8_r0) >> page_shift) - key_lo_page, n_pages - 1)];
+    id8 = pg_lds[min(page_of(kt * C::BN + l8_r0) - key_lo_page, n_pages - 1)];
   };
   auto fp8_load_scalar = [&](int tk, int tv) {
     const int t = l8_v ? tv : tk;
@@ -630,7 +643,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     const uint32_t bytes = (tile_ok && good) ? (uint32_t)rows * (uint32_t)token_bytes : 0u;
     const uint64_t addr = reinterpret_cast<uint64_t>(l8_v ? vbase : kbase) +
                           (good ? (uint64_t)(uint32_t)id8 * (uint64_t)page_bytes : 0) +
-                          (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
+                          (uint64_t)(uint32_t)(row_in_page(key0) * (int)token_bytes);
 #pragma unroll
     for (int j = 0; j < kLoads8; ++j) {
       const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)addr, j);
@@ -645,7 +658,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     read_ids8(tk + 1, tv + 1);
   };
   auto fp8_load = [&](int tk, int tv) {
-    if constexpr (FP8 && MODE == kPagesScalar) {
+    if constexpr (FP8 && kScalar) {
       fp8_load_scalar(tk, tv);
     } else {
 #pragma unroll
@@ -678,7 +691,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   auto page_slot = [&](int t, int i) {
     const int kt = kt0 + min(max(t, 0), n_tiles - 1);
     const int key0 = kt * C::BN + (i * IW + iw) * C::KPI;
-    return min((key0 >> page_shift) - key_lo_page, n_pages - 1);
+    return min(page_of(key0) - key_lo_page, n_pages - 1);
   };
   constexpr int kLoads = 2 * NCHT;
   const int lj = min(lane, kLoads - 1);  // the load this lane prepares (lanes past kLoads: a copy)
@@ -703,7 +716,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     const uint64_t off = good ? (uint64_t)(uint32_t)id * (uint64_t)page_bytes : 0;
     const int rows = min(max(rq.kv_len - key0, 0), C::KPI);
     const uint32_t bytes = (tile_ok && good) ? (uint32_t)rows * (uint32_t)token_bytes : 0u;
-    const uint64_t addr = base + off + (uint64_t)(uint32_t)((key0 & (page_size - 1)) * (int)token_bytes);
+    const uint64_t addr = base + off + (uint64_t)(uint32_t)(row_in_page(key0) * (int)token_bytes);
     const uint32_t lds =
         lds0 + (uint32_t)(((lj_v ? C::NBUF : 0) + (t & (C::NBUF - 1))) * C::TILE_BYTES + (lj_i * IW + iw) * 1024);
 #pragma unroll
@@ -722,10 +735,10 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     read_ids(t + 1);
   };
   auto issue = [&](int t) {  // bf16: load group t
-    if constexpr (MODE == kPagesScalar) issue_group_scalar(t);
+    if constexpr (kScalar) issue_group_scalar(t);
     else issue_group(t);
   };
-  constexpr int kGroupLoads = MODE == kPagesScalar ? kLoads : NCHT + NCHV;  // one thread's loads of a group
+  constexpr int kGroupLoads = kScalar ? kLoads : NCHT + NCHV;  // one thread's loads of a group
 
   // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
@@ -997,7 +1010,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     // the sequence is the plain one: O = alpha(t) O, then O += PV(t). A slot is rewritten
     // two iterations after it was filled, one barrier after wave 4 read it.
     if (issuer) {
-      if constexpr (MODE == kPagesScalar) {
+      if constexpr (kScalar) {
         read_ids(-C::NBUF);
 #pragma unroll
         for (int t = -C::NBUF; t < 0; ++t) issue_group_scalar(t);
@@ -1028,7 +1041,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     };
     auto spec_iter = [&](int t, f32x4 (&sc)[C::KB][NB], f32x4 (&sn)[C::KB][NB]) {
       if (issuer) {
-        if constexpr (MODE == kPagesScalar) issue_group_scalar(t);
+        if constexpr (kScalar) issue_group_scalar(t);
         else issue_group(t);
       }
       if (s_rows) {
@@ -1060,7 +1073,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
   } else if constexpr (!kPP) {
     if constexpr (FP8) {
-      if constexpr (MODE == kPagesScalar) read_ids8(0, -2);  // the first group's page ids
+      if constexpr (kScalar) read_ids8(0, -2);  // the first group's page ids
 #pragma unroll
       for (int t = -C::NBUF; t < -1; ++t) {
         fp8_load(t + C::NBUF, t + C::NBUF - 2);
@@ -1069,7 +1082,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       fp8_load(C::NBUF - 1, C::NBUF - 3);  // group -1, stored in iteration 0
     } else {
       if (issuer) {
-        if constexpr (MODE == kPagesScalar) {
+        if constexpr (kScalar) {
           read_ids(-C::NBUF);
 #pragma unroll
           for (int t = -C::NBUF; t < 0; ++t) issue_group_scalar(t);
@@ -1092,7 +1105,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         fp8_load(t + C::NBUF, t + C::NBUF - 2);       // group t
         // with two buffers the tiles just stored, K(t + 1) and V(t - 1), are this iteration's
         if constexpr (C::NBUF == 2) __syncthreads();
-      } else if constexpr (MODE == kPagesScalar) {
+      } else if constexpr (kScalar) {
         if (issuer) issue_group_scalar(t);
       } else {
         if (issuer) issue_group(t);
@@ -1155,7 +1168,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       // acknowledgement is due only at the trailing waves' wait for group -2.
       if (!q_ready) load_q();
       q_ready = false;
-      if constexpr (MODE == kPagesScalar) {
+      if constexpr (kScalar) {
         read_ids(-3);
         issue_group_scalar(-3);
       } else {
@@ -1192,12 +1205,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
           float alpha[NB];
           softmax(s, pb, alpha, std::true_type{});
         }
-        if constexpr (MODE == kPagesScalar) prep(t + 1);
+        if constexpr (kScalar) prep(t + 1);
         // A(t) reads group t-2; the leading group's A(t) starts at the next barrier, the
         // trailing group's one phase later (its wait for group t-1 follows its A(t))
         if (leading) wait_vmcnt<2 * kGroupLoads>();
         __syncthreads();
-        if constexpr (MODE == kPagesScalar) {
+        if constexpr (kScalar) {
           if (has_rows) {
             pv_acc(pb, t, [&](int st) {
               if (st % kEvery == 0 && st / kEvery < kLoads) fire(st / kEvery);
@@ -1298,6 +1311,7 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
     if (fp8) {  // one fp8 schedule: NARROW changes nothing in it
       constexpr int kRowsPerLoad8 = 64 / (D / 8);  // key rows of one wave's fp8 load
       if (pow2 && P >= kRowsPerLoad8) return launch_one<D, true, NB, false, kPagesScalar>(a, stream);
+      if (P % kRowsPerLoad8 == 0) return launch_one<D, true, NB, false, kPagesScalarDiv>(a, stream);
       return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, false, kPagesPow2>(a, stream)
                                          : launch_one<D, true, NB, false, kPagesGeneral>(a, stream);
     }
@@ -1309,6 +1323,7 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   // descriptors.
   if constexpr (!NARROW && waves_for(D) == 8) {
     if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, NARROW, kPagesScalar>(a, stream);
+    if (P % Geo<D, NB>::KPI == 0) return launch_one<D, false, NB, NARROW, kPagesScalarDiv>(a, stream);
   } else if constexpr (NARROW && waves_for(D) == 8 && D >= 128) {
     // A narrow launch of at most one unit per two compute units splits head_dim in PV over
     // two workgroups per unit (same bits). A CU streams a unit's gather at a rate of its own,
