@@ -169,6 +169,12 @@ dpp_status launch_passes(const dpp_plan* plan, const void* q, const void* k_pool
     return m == 0.5f && e - 1 >= -64 && e - 1 <= 64;
   };
   a.kv_scale_pow2 = pow2_in_range(a.k_scale) && pow2_in_range(a.v_scale) ? 1 : 0;
+  {
+    const int64_t token_bytes = (int64_t)plan->cfg.num_kv_heads * plan->cfg.head_dim *
+                                (plan->cfg.kv_dtype == DPP_KV_FP8_E4M3 ? 1 : 2);
+    const int64_t pool = plan->ragged ? -1 : num_pages * plan->cfg.page_size * token_bytes;
+    a.pool_bytes = pool >= 0 && pool < (int64_t)0xFFFFFFC0u ? (uint32_t)pool : 0u;
+  }
 
   MergeArgs m{};
   m.header = a.header;

@@ -199,6 +199,7 @@ struct PrefillArgs {
   float k_scale;
   float v_scale;
   int32_t kv_scale_pow2;    // fp8: both scales are powers of two in [2^-64, 2^64]
+  uint32_t pool_bytes;      // bytes of one pool (num_pages x page bytes) if below 2^32 - 64, else 0
 };
 
 struct MergeArgs {

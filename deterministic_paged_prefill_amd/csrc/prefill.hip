@@ -248,7 +248,10 @@ __device__ inline void wait_vmcnt() {
 //                  registers
 //   kPagesScalarDiv the same for any other page size holding whole loads (page and row of a
 //                  key by division)
-constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2, kPagesScalarDiv = 3;
+//   kPagesOff32    kPagesPow2's per-lane pages, for a pool of at most 4 GiB: one buffer
+//                  descriptor per tensor and unit, and a 32-bit offset per lane (past kv_len or
+//                  on an invalid page an offset past the descriptor's range, which reads zeros)
+constexpr int kPagesGeneral = 0, kPagesPow2 = 1, kPagesScalar = 2, kPagesScalarDiv = 3, kPagesOff32 = 4;
 
 // NB: 16-row blocks per wave. VH (narrow bf16 kernel only): the launch runs every unit on two
 // workgroups, one per half of head_dim in PV. Both compute the unit's scores and softmax from
@@ -485,6 +488,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   //         swizzled slot.
   //   fp8:  chunk q = tid + THREADS i, loaded to registers, decoded, stored to its slot.
   constexpr bool pow2_pages = MODE != kPagesGeneral;
+  constexpr bool kLanePow2 = MODE == kPagesPow2 || MODE == kPagesOff32;  // per-lane, power-of-two pages
   // (fp8 with scalar pages: register loads through buffer descriptors, see fp8_load)
   // Waves that issue DMA loads: 2, 3, 6, 7 in the narrow bf16 kernel, otherwise all.
   constexpr int IW = kSpec ? 4 : C::WAVES;
@@ -521,8 +525,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
     kcol[i] = c_k * 8 * kElem;
     vcol[i] = c_v * 8 * kElem;
-    pg_rel[i] = MODE == kPagesPow2 ? (krow[i] >> page_shift) : 0;
-    in_page[i] = MODE == kPagesPow2 ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
+    pg_rel[i] = kLanePow2 ? (krow[i] >> page_shift) : 0;
+    in_page[i] = kLanePow2 ? (int64_t)(krow[i] & (page_size - 1)) * token_bytes : 0;
   }
   // V chunks: the same as K's, or, VH, the chunks of this workgroup's half rows (8 key rows
   // of 128 bytes per wave-wide load at D = 128)
@@ -542,8 +546,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       vrow[i] = krow[i];
       vcolh[i] = vcol[i];
     }
-    vpg_rel[i] = MODE == kPagesPow2 ? (vrow[i] >> page_shift) : 0;
-    vin_page[i] = MODE == kPagesPow2 ? (int64_t)(vrow[i] & (page_size - 1)) * token_bytes : 0;
+    vpg_rel[i] = kLanePow2 ? (vrow[i] >> page_shift) : 0;
+    vin_page[i] = kLanePow2 ? (int64_t)(vrow[i] & (page_size - 1)) * token_bytes : 0;
   }
   // scalar pages: byte offset of the lane's chunk from its load's first key row
   int voff_k[NCHT], voff_v[NCHT];
@@ -595,12 +599,24 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       int32_t pid[N];
 #pragma unroll
       for (int i = 0; i < N; ++i) pid[i] = pg_lds[tp + pgr[i]];
+      if constexpr (MODE == kPagesOff32) {
+        // the tensor's descriptor from this kv head's base over the rest of the pool
+        const i32x4 rsrc = buffer_rsrc(uniform64(reinterpret_cast<uint64_t>(base)),
+                                       (uint32_t)__builtin_amdgcn_readfirstlane((int)(a.pool_bytes - (uint32_t)(kvh * D * kElem))));
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const bool ok = rows[i] < lim && pid[i] >= 0 && pid[i] < a.num_pages;
-        const uint64_t off = (uint64_t)(uint32_t)(ok ? pid[i] : 0) * (uint64_t)page_bytes +
-                             (uint64_t)inp[i] + (uint64_t)cols[i];
-        dma16(ok ? base + off : zero16, buf + (uint32_t)((i * IW + iw) * 1024));
+        for (int i = 0; i < N; ++i) {
+          const bool ok = rows[i] < lim && pid[i] >= 0 && pid[i] < a.num_pages;
+          const uint32_t off = (uint32_t)pid[i] * (uint32_t)page_bytes + (uint32_t)inp[i] + (uint32_t)cols[i];
+          dma16_buf((int)(ok ? off : 0xFFFFFFF0u), rsrc, buf + (uint32_t)((i * IW + iw) * 1024));
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) {
+          const bool ok = rows[i] < lim && pid[i] >= 0 && pid[i] < a.num_pages;
+          const uint64_t off = (uint64_t)(uint32_t)(ok ? pid[i] : 0) * (uint64_t)page_bytes +
+                               (uint64_t)inp[i] + (uint64_t)cols[i];
+          dma16(ok ? base + off : zero16, buf + (uint32_t)((i * IW + iw) * 1024));
+        }
       }
     } else {
 #pragma unroll
@@ -1324,6 +1340,8 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
   if constexpr (!NARROW && waves_for(D) == 8) {
     if (pow2 && P >= Geo<D, NB>::KPI) return launch_one<D, false, NB, NARROW, kPagesScalar>(a, stream);
     if (P % Geo<D, NB>::KPI == 0) return launch_one<D, false, NB, NARROW, kPagesScalarDiv>(a, stream);
+    // smaller power-of-two pages of a pool within 4 GiB: 32-bit per-lane offsets
+    if (pow2 && P <= BNX && a.pool_bytes > 0) return launch_one<D, false, NB, NARROW, kPagesOff32>(a, stream);
   } else if constexpr (NARROW && waves_for(D) == 8 && D >= 128) {
     // A narrow launch of at most one unit per two compute units splits head_dim in PV over
     // two workgroups per unit (same bits). A CU streams a unit's gather at a rate of its own,
