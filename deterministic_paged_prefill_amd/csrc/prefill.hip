@@ -673,9 +673,31 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     }
     read_ids8(tk + 1, tv + 1);
   };
+  // fp8 with per-lane pages of a pool within 4 GiB: register loads through one descriptor per
+  // tensor at a 32-bit offset per lane (past kv_len or on an invalid page: past its range)
+  auto fp8_off32 = [&](int col, int row, int t) -> int {
+    const int kt = kt0 + min(max(t, 0), n_tiles - 1);
+    const int key = kt * C::BN + row;
+    const int pid = pg_lds[((kt * C::BN) >> page_shift) - key_lo_page + (row >> page_shift)];
+    const bool ok = t >= 0 && t < n_tiles && key < rq.kv_len && pid >= 0 && pid < a.num_pages;
+    const uint32_t off = (uint32_t)pid * (uint32_t)page_bytes + (uint32_t)((row & (page_size - 1)) * (int)token_bytes) +
+                         (uint32_t)col;
+    return (int)(ok ? off : 0xFFFFFFF0u);
+  };
   auto fp8_load = [&](int tk, int tv) {
     if constexpr (FP8 && kScalar) {
       fp8_load_scalar(tk, tv);
+    } else if constexpr (FP8 && MODE == kPagesOff32) {
+      const int nrec = __builtin_amdgcn_readfirstlane((int)(a.pool_bytes - (uint32_t)(kvh * D * kElem)));
+      const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(uniform64(reinterpret_cast<uint64_t>(kbase))), (short)0, nrec, 0x00020000);
+      const __amdgpu_buffer_rsrc_t rvs = __builtin_amdgcn_make_buffer_rsrc(
+          reinterpret_cast<void*>(uniform64(reinterpret_cast<uint64_t>(vbase))), (short)0, nrec, 0x00020000);
+#pragma unroll
+      for (int i = 0; i < C::NCH; ++i) {
+        kreg[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk, fp8_off32(kcol[i], krow[i], tk), 0, 0));
+        vreg[i] = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rvs, fp8_off32(vcol[i], krow[i], tv), 0, 0));
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < C::NCH; ++i) {
@@ -1328,6 +1350,7 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
       constexpr int kRowsPerLoad8 = 64 / (D / 8);  // key rows of one wave's fp8 load
       if (pow2 && P >= kRowsPerLoad8) return launch_one<D, true, NB, false, kPagesScalar>(a, stream);
       if (P % kRowsPerLoad8 == 0) return launch_one<D, true, NB, false, kPagesScalarDiv>(a, stream);
+      if (pow2 && P <= block_n_for(D) && a.pool_bytes > 0) return launch_one<D, true, NB, false, kPagesOff32>(a, stream);
       return pow2 && P <= block_n_for(D) ? launch_one<D, true, NB, false, kPagesPow2>(a, stream)
                                          : launch_one<D, true, NB, false, kPagesGeneral>(a, stream);
     }
