@@ -15,8 +15,10 @@ value     extend KV GB/s: 16 requests, each extending 1-4 tokens behind a 1024-t
 prefill   cold 16 x 1028-token causal prefill, same shapes: causal FLOPs / step time.
 others    the remaining configurations, each timed and its cached-vs-full bits checked: the
           67-token prompt (full prefill vs 3-token extend, latency), the mixed batch (3,700-token
-          prefill + 7 cached tails, causal TFLOP/s) and the long fp8 path (24/4/256, 8k and 32k
-          prefills and a 1k extend behind 31k cached keys: TFLOP/s and workspace bytes).
+          prefill + 7 cached tails, causal TFLOP/s), the long fp8 path (24/4/256, 8k and 32k
+          prefills and a 1k extend behind 31k cached keys: TFLOP/s and workspace bytes),
+          head_dim 512 (16/4/512 prefill and extends) and the cold prefill at page sizes 1, 2,
+          12 and 16 (TFLOP/s).
 decode    8 one-token decodes over 8k-128k keys each (same shapes, 2-32 KV splits a row, the
           split partials merged): logical KV bytes / step time (1.4 GB of KV, far past the
           Infinity Cache).
@@ -533,6 +535,18 @@ def main() -> int:
             "prefill_us": round(ms6f * 1e3, 2), "prefill_causal_flops": fl6,
             "prefill_tflops": round(fl6 / (ms6f * 1e-3) / 1e12, 2), "extend_us": round(ms6e * 1e3, 2),
             "cached_vs_full_max_abs_diff": bits_equal(b6e, o6e, l6e, b6f, o6f, l6f, [(i, i) for i in range(4)])}
+        log("page sizes")
+        pages = {}
+        for page in (1, 2, 12, 16):
+            w7 = wl.cold_prefill(page_size=page)
+            b7 = w7.batches["full"]
+            ms7, _, _, _ = timed_leg(w7, b7, 20, 20)
+            pages[str(page)] = round(causal_flops(b7, hq, d) / (ms7 * 1e-3) / 1e12, 2)
+            del w7
+        others["page_sizes"] = {
+            "workload": "the cold 16 x 1,028 prefill (32/8/128 bf16) with its KV in pages of 1, 2, 12 and 16 tokens "
+                        "(page ids shuffled): causal TFLOP/s per page size",
+            "tflops": pages}
 
     ext = result["extend"]
     traffic = traffic_from_profile(ext["alg_bytes"])
