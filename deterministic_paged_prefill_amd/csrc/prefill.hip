@@ -1371,9 +1371,13 @@ hipError_t launch_nb(const PrefillArgs& a, bool fp8, hipStream_t stream) {
     // so two CUs that each load all of K and half of V (3/4 of the unit's bytes) finish sooner
     // than one that loads all of it, while the K they share comes from HBM once.
     if (2 * a.num_items * a.num_kv_heads <= compute_units()) {
+      if (pow2 && P <= BNX && a.pool_bytes > 0) return launch_one<D, false, NB, NARROW, kPagesOff32, true, BNX>(a, stream);
       return pow2 && P <= BNX ? launch_one<D, false, NB, NARROW, kPagesPow2, true, BNX>(a, stream)
                               : launch_one<D, false, NB, NARROW, kPagesGeneral, true, BNX>(a, stream);
     }
+  }
+  if constexpr (NARROW) {
+    if (pow2 && P <= BNX && a.pool_bytes > 0) return launch_one<D, false, NB, NARROW, kPagesOff32, false, BNX>(a, stream);
   }
   return pow2 && P <= BNX ? launch_one<D, false, NB, NARROW, kPagesPow2, false, BNX>(a, stream)
                           : launch_one<D, false, NB, NARROW, kPagesGeneral, false, BNX>(a, stream);
