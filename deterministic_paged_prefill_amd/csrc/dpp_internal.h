@@ -37,6 +37,9 @@ constexpr int kNarrowRows = 16;
 // Keys per KV tile. Tiles start at absolute key positions 0, BN, 2BN, ...
 DPP_HOST_DEVICE constexpr int block_n_for(int head_dim) { return head_dim <= 128 ? 64 : 32; }
 constexpr int kMaxBlockM = 256;
+// Largest group (q heads per kv head): the kernels split a packed row into (token, q head)
+// with a multiply-shift that is exact for groups up to this size.
+constexpr int kMaxGroup = 1024;
 // LDS of a workgroup: a ring of K and V tiles (bf16) -- four of each, two at head_dim 512
 // whose 32-key tiles are 32 KiB -- then page-id tables (4 bytes an entry; two in a persistent
 // launch, one per unit in flight), within the 160 KiB of a CU.

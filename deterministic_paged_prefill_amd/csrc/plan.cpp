@@ -234,6 +234,8 @@ extern "C" dpp_status dpp_plan_create_ex(const dpp_config* cfg, int32_t batch_si
     return fail(DPP_ERR_UNSUPPORTED,
                 "num_qo_heads must be a positive multiple of num_kv_heads (got " +
                     std::to_string(c.num_qo_heads) + "/" + std::to_string(c.num_kv_heads) + ")");
+  if (c.num_qo_heads / c.num_kv_heads > kMaxGroup)
+    return fail(DPP_ERR_UNSUPPORTED, "num_qo_heads / num_kv_heads must be at most " + std::to_string(kMaxGroup));
   if (c.head_dim != 64 && c.head_dim != 128 && c.head_dim != 256 && c.head_dim != 512)
     return fail(DPP_ERR_UNSUPPORTED, "head_dim " + std::to_string(c.head_dim) +
                                          " not built (64, 128, 256 and 512 are)");

@@ -352,6 +352,24 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   const int lg = lane >> 4;                // 16-lane group: 8-wide k slice in, 4 output rows out
   const int li = lane & 15;                // column (query row) within a 16-row block
   const int row_wave = kSpec ? 0 : wave;  // whose 16-row blocks this wave works on
+  // Packed row R = R0 + off of a wave (R0 = the tile's first row + RPW * row_wave, 0 <= off <
+  // RPW) is token t0 + q of q head h0 + off - q g, with (t0, h0) = divmod(R0, g) once per
+  // unit and q = (h0 + off) / g taken as (h0 + off) * ceil(2^24 / g) >> 24. That quotient is
+  // exact while (h0 + off) * g < 2^24, which g <= 1024 (checked by the planner) keeps.
+  const uint32_t g_magic = ((1u << 24) + (uint32_t)g - 1u) / (uint32_t)g;
+  struct RowPos {
+    int token, head;  // token of the request's query, q head within the kv head's group
+  };
+  auto row_base = [&](int row_start) {  // (t0, h0) of this wave's rows of a tile at row_start
+    const int r0 = row_start + row_wave * C::RPW;
+    const int t0 = r0 / g;
+    return RowPos{t0, r0 - t0 * g};
+  };
+  auto row_pos = [&](RowPos b, int off) {
+    const int x = b.head + off;
+    const int q = (int)(((uint32_t)x * g_magic) >> 24);
+    return RowPos{b.token + q, x - q * g};
+  };
   const int page_size = a.page_size;
   const int page_shift = (page_size & (page_size - 1)) == 0 ? __builtin_ctz(page_size) : -1;
   // page of a key and the key's row in it (scalar page modes)
@@ -399,10 +417,11 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     s_rows = has_rows && (!kSpec || wave == 0);  // scores and softmax
     o_rows = has_rows && (!kSpec || wave == 4);  // output
     // Rows of this lane: tile-local packed row lr = RPW*wave + 16*nb + li.
+    const RowPos rb = row_base(it.row_start);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int lr = row_wave * C::RPW + nb * 16 + li;
-      p_row[nb] = lr < tile_rows ? ctx + (it.row_start + lr) / g : INT_MAX;
+      p_row[nb] = lr < tile_rows ? ctx + row_pos(rb, nb * 16 + li).token : INT_MAX;
     }
     p_min = ctx + it.row_start / g;
     kt0 = it.kv_tile_begin;
@@ -432,14 +451,14 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   // ---- query rows as the QK^T B operand: lane (lg, li) holds head_dim [32dc + 8lg, +8)
   bf16x8 qreg[NB][C::DC];
   auto load_q = [&]() {
+    const RowPos rb = row_base(it.row_start);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int lr = row_wave * C::RPW + nb * 16 + li;
       const bool valid = lr < tile_rows && s_rows;
-      const int R = it.row_start + lr;
-      const int token = R / g;
+      const RowPos rp = row_pos(rb, nb * 16 + li);
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((int64_t)(rq.q_start + token) * a.num_qo_heads + kvh * g + (R - token * g)) * D + 8 * lg;
+                           ((int64_t)(rq.q_start + rp.token) * a.num_qo_heads + kvh * g + rp.head) * D + 8 * lg;
 #pragma unroll
       for (int dc = 0; dc < C::DC; ++dc) {
         u32x4 v = u32x4{0u, 0u, 0u, 0u};
@@ -453,14 +472,14 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
   auto load_q_of = [&](const UnitRecord& u) {
     const int u_rows = min(C::PLAN_BM, u.req.qo_len * g - u.row_start);
     const bool w_rows = row_wave * C::RPW < u_rows;  // has_rows of that unit
+    const RowPos rb = row_base(u.row_start);
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int lr = row_wave * C::RPW + nb * 16 + li;
       const bool valid = lr < u_rows && w_rows;
-      const int R = u.row_start + lr;
-      const int token = R / g;
+      const RowPos rp = row_pos(rb, nb * 16 + li);
       const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) +
-                           ((int64_t)(u.req.q_start + token) * a.num_qo_heads + u.kv_head * g + (R - token * g)) * D +
+                           ((int64_t)(u.req.q_start + rp.token) * a.num_qo_heads + u.kv_head * g + rp.head) * D +
                            8 * lg;
 #pragma unroll
       for (int dc = 0; dc < C::DC; ++dc) {
@@ -820,21 +839,21 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     const int e_rows = min(C::PLAN_BM, e.req.qo_len * g - e.row_start);
     const int e_ctx = e.req.kv_len - e.req.qo_len;
     const int e_key0 = e.split * kSplitTokens;
-    // output row (packed row R of the request) in o and lse
-    auto out_row = [&](int lr) {
-      const int R = e.row_start + lr;
-      const int token = R / g;
-      return (int64_t)(e.req.q_start + token) * a.num_qo_heads + e.kv_head * g + (R - token * g);
+    const RowPos rb = row_base(e.row_start);
+    // output row (in o and lse) of a row at (token, q head)
+    auto out_row = [&](RowPos rp) {
+      return (int64_t)(e.req.q_start + rp.token) * a.num_qo_heads + e.kv_head * g + rp.head;
     };
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
       const int lr = row_wave * C::RPW + nb * 16 + li;  // the row this lane holds
-      const int p = lr < e_rows ? e_ctx + (e.row_start + lr) / g : -1;
+      const RowPos pos = row_pos(rb, nb * 16 + li);
+      const int p = lr < e_rows ? e_ctx + pos.token : -1;
       const bool mine = p >= e_key0;                   // a row of this split
       const float inv_l = 1.f / l_sum[nb];
       const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l_sum[nb]);
       if (mine && p < kSplitTokens) {
-        const int64_t orow = out_row(lr);
+        const int64_t orow = out_row(pos);
         if (lg == 0 && vh == 0) lse_out[orow] = lse2 * kLn2;
         if constexpr (!kPP) {
           DPP_GLOBAL uint16_t* op = o_out + orow * D + vh * (D / 2) + 4 * lg;
@@ -858,30 +877,41 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
         if (lg == 0 && vh == 0) part_lse_out[slot] = lse2;
       }
       if constexpr (kPP) {
-#pragma unroll
-      for (int sp = 0; sp < VDB / 4; ++sp) {  // head_dim [64 sp, +64)
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          const int db = 4 * sp + k;
-          const int c = (2 * k + (lg >> 1)) ^ (li & 7);
-          *reinterpret_cast<DPP_LDS u32x2*>((DPP_LDS unsigned char*)stage + li * 128 + c * 16 + (lg & 1) * 8) =
-              u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
-                    pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
-        }
-        asm volatile("" ::: "memory");  // the wave's own LDS writes, then its reads (in order)
+        // the two staged rows this lane stores, r = 8h + lane / 8, from 16-byte piece kk
+        const int kk = lane & 7;
+        int64_t srow[2];
+        bool sok[2];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-          const int r = 8 * h + (lane >> 3);  // staged row, 16-byte piece kk of its 128 bytes
-          const int kk = lane & 7;
-          const u32x4 v = *reinterpret_cast<const DPP_LDS u32x4*>((const DPP_LDS unsigned char*)stage + r * 128 +
-                                                                  ((kk ^ (r & 7)) << 4));
-          const int rlr = row_wave * C::RPW + nb * 16 + r;
-          const int rp = rlr < e_rows ? e_ctx + (e.row_start + rlr) / g : -1;
-          if (rp >= e_key0 && rp < kSplitTokens)
-            *reinterpret_cast<DPP_GLOBAL u32x4*>(o_out + out_row(rlr) * D + 64 * sp + 8 * kk) = v;
+          const int r = 8 * h + (lane >> 3);
+          const RowPos rp = row_pos(rb, nb * 16 + r);
+          const int p_r = row_wave * C::RPW + nb * 16 + r < e_rows ? e_ctx + rp.token : -1;
+          sok[h] = p_r >= e_key0 && p_r < kSplitTokens;
+          srow[h] = out_row(rp) * D + 8 * kk;
         }
-        asm volatile("" ::: "memory");
-      }
+#pragma unroll
+        for (int sp = 0; sp < VDB / 4; ++sp) {  // head_dim [64 sp, +64)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int db = 4 * sp + k;
+            const int c = (2 * k + (lg >> 1)) ^ (li & 7);
+            *reinterpret_cast<DPP_LDS u32x2*>((DPP_LDS unsigned char*)stage + li * 128 + c * 16 + (lg & 1) * 8) =
+                u32x2{pack_bf16x2(acc[db][nb][0] * inv_l, acc[db][nb][1] * inv_l),
+                      pack_bf16x2(acc[db][nb][2] * inv_l, acc[db][nb][3] * inv_l)};
+          }
+          asm volatile("" ::: "memory");  // the wave's own LDS writes, then its reads (in order)
+          u32x4 v[2];
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int r = 8 * h + (lane >> 3);
+            v[h] = *reinterpret_cast<const DPP_LDS u32x4*>((const DPP_LDS unsigned char*)stage + r * 128 +
+                                                           ((kk ^ (r & 7)) << 4));
+          }
+#pragma unroll
+          for (int h = 0; h < 2; ++h)
+            if (sok[h]) *reinterpret_cast<DPP_GLOBAL u32x4*>(o_out + srow[h] + 64 * sp) = v[h];
+          asm volatile("" ::: "memory");
+        }
       }
     }
   };

@@ -73,7 +73,7 @@ typedef enum { DPP_KV_BF16 = 0, DPP_KV_FP8_E4M3 = 1 } dpp_kv_dtype;
 
 /* Model-level constants. These, and only these, fix the arithmetic of every row. */
 typedef struct {
-  int32_t num_qo_heads;  /* Hq, a multiple of num_kv_heads */
+  int32_t num_qo_heads;  /* Hq, a multiple of num_kv_heads, at most 1024 x it */
   int32_t num_kv_heads;  /* Hkv */
   int32_t head_dim;      /* 64, 128, 256 or 512 */
   int32_t page_size;     /* tokens per page, 1..1024; 0 = ragged (contiguous) KV */

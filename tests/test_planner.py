@@ -425,6 +425,7 @@ def test_malformed_batches_are_rejected(dpp, mutate, status):
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=96), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=1024), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=30, num_kv_heads=8, head_dim=128), "DPP_ERR_UNSUPPORTED"),
+    (dict(num_qo_heads=2050, num_kv_heads=2, head_dim=128), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=-1), "DPP_ERR_UNSUPPORTED"),
     (dict(num_qo_heads=32, num_kv_heads=8, head_dim=128, page_size=1025), "DPP_ERR_UNSUPPORTED"),
 ])
@@ -782,3 +783,15 @@ def test_run_static_refuses_plans_above_its_scratch(dpp):
     assert st == dpp.DPP_ERR_SHAPE  # dpp_run's argument checks come first
     st = lib.dpp_run_static(small._h, fake, 8192, fake, fake, 600, fake, 512, fake, fake, 2, None)
     assert st == dpp.DPP_ERR_INVALID
+
+
+def test_row_split_multiply_shift_is_exact():
+    """The kernels split packed row R0 + off of a wave into (token, q head) with
+    (h0 + off) * ceil(2^24 / g) >> 24 in place of (h0 + off) / g, for h0 < g, off < 32 and
+    g up to the planner's limit of 1024; that quotient must be exact and the product must fit
+    in 32 bits."""
+    for g in range(1, 1025):
+        m = ((1 << 24) + g - 1) // g
+        x = np.arange(0, g + 32, dtype=np.uint64)
+        assert (x * m < 2**32).all()
+        assert ((x * m) >> 24 == x // g).all()
