@@ -1222,6 +1222,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     int32_t rcur = rv, rnext = 0, rfetch = 0;
     bool has_prev = false, rotate = false;
     bool q_ready = false;  // this unit's Q was loaded in the previous unit's last A phase
+    constexpr bool kLateQ = D <= 128;
     if (cur_next >= 0) rnext = fetch_record(cur_next);
     wait_vmcnt<0>();
     __syncthreads();  // the first unit's page ids visible
@@ -1293,7 +1294,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
           if (has_rows) pv_acc(pb, t, no_hook);
         }
         if (has_rows && t + 1 < n_tiles) qk(s, t + 1);
-        if (t == n_tiles - 1 && has_next) {
+        if (t == n_tiles - 1 && has_next && !(kLateQ && leading)) {
           // The last QK^T of this unit ran in A(t-1): its Q registers take the next unit's
           // Q now, in flight during the output write and the transition.
           load_q_of(decode(rnext));
@@ -1306,6 +1307,13 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       if (leading) {
         if (has_rows) write_out(rcur);
         reset_state();
+        // At head_dim <= 128 the leading waves load the next unit's Q after their write: a wait
+        // for the write's own memory operations (a register reload) would otherwise wait for
+        // these loads as well. (At 256 the code generated for that order is slower.)
+        if (kLateQ && has_next) {
+          load_q_of(decode(rnext));
+          q_ready = true;
+        }
         __syncthreads();
       }
       if (!has_next) {
