@@ -168,11 +168,18 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
 // x[l | 16]} and permlane32_swap(x, x) the pair {x[l & 31], x[(l & 31) + 32]}, always in that
 // order, so each lane of a row combines the same operands in the same order and ends with the
 // same bits: ((x0 + x1) + (x2 + x3)) for the sum.
+// Maximum of two scores (never NaN) as one instruction: fmaxf would first quiet each operand
+// it cannot prove canonical (max(x, x)), which is every value from a lane swap.
+__device__ inline float max2(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
 __device__ inline float row_max4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ inline float row_sum4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -966,11 +973,12 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
     bool moved = false;
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) {
-      float mx = s[0][nb][0];
+      // the 4 KB scores of the lane's row: max3 over the first three, then two at a time
+      // (from -inf, pairwise: max3 instructions with no quieting of the scores)
+      float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < C::KB; ++kb)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) mx = fmaxf(mx, s[kb][nb][j]);
+      for (int e = 0; e < 4 * C::KB; e += 2)
+        mx = fmaxf(fmaxf(mx, s[e / 4][nb][e % 4]), s[(e + 1) / 4][nb][(e + 1) % 4]);
       mx = row_max4(mx);
       // The reference max moves only when this tile's max exceeds it by more than kRebase
       // (and on the row's first keys); otherwise P_j <= 2^kRebase and O, l keep their scale.
