@@ -19,9 +19,11 @@
 //            would change no bit there).
 //   softmax  online, fp32, base 2, with a lazily moved reference max r (c = sm_scale log2 e):
 //            t = c max_j s_j; if t > r + 8 then r' = t, alpha = exp2(r - r') else r' = r,
-//            alpha = 1; P_j = exp2(fma(s_j, c, -r')) (so P_j <= 2^8); l = fma(l, alpha, sum_j P_j);
-//            O = alpha O. Row max and row sum: one fixed pairwise tree over the lane's values,
-//            then a butterfly over the four lanes holding the row.
+//            alpha = 1; P_j = exp2(fma(s_j, c, -r')) (so P_j <= 2^8); O = alpha O. Row max: a
+//            fixed max3 chain over the lane's values, then a butterfly over the four lanes
+//            holding the row. Row sum: each of the four lanes keeps its own share,
+//            l_lane = fma(l_lane, alpha, pairwise tree of its P_j); after the split's last
+//            tile l = (l_0 + l_1) + (l_2 + l_3) by the same butterfly.
 //   PV       O^T[d, row] = alpha O^T + V^T P^T on the same MFMA, P rounded to bf16 (RNE). The
 //            V^T operand comes straight from the natural layout through ds_read_tr16_b64.
 // After a split's last tile a row writes o = O / l (bf16) and lse = (r + log2 l) ln 2, or, if
@@ -806,7 +808,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
 
   // ---- online-softmax state of this lane's rows
   const float c = a.scale_log2;
-  float m_sc[NB], l_sum[NB];  // reference max (scaled, base 2) and running sum per row
+  float m_sc[NB], l_sum[NB];  // reference max (scaled, base 2) per row; this lane's share of its sum
   f32x4 acc[VDB][NB];
   auto reset_state = [&]() {
 #pragma unroll
@@ -857,8 +859,9 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       const RowPos pos = row_pos(rb, nb * 16 + li);
       const int p = lr < e_rows ? e_ctx + pos.token : -1;
       const bool mine = p >= e_key0;                   // a row of this split
-      const float inv_l = 1.f / l_sum[nb];
-      const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l_sum[nb]);
+      const float l = row_sum4(l_sum[nb]);  // the row's sum from the four lanes' shares
+      const float inv_l = 1.f / l;
+      const float lse2 = m_sc[nb] + __builtin_amdgcn_logf(l);
       if (mine && p < kSplitTokens) {
         const int64_t orow = out_row(pos);
         if (lg == 0 && vh == 0) lse_out[orow] = lse2 * kLn2;
@@ -993,7 +996,8 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       for (int kb = 0; kb < C::KB; ++kb)
 #pragma unroll
         for (int j = 0; j < 4; ++j) pv[kb][j] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][nb][j], c, -m_use));
-      // row sum: pairs within each 4-key group, then a pairwise tree over the groups
+      // this lane's share of the row sum: pairs within each 4-key group, then a pairwise tree
+      // over the groups
       float ts[C::KB];
 #pragma unroll
       for (int kb = 0; kb < C::KB; ++kb) ts[kb] = (pv[kb][0] + pv[kb][1]) + (pv[kb][2] + pv[kb][3]);
@@ -1001,8 +1005,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       for (int h = C::KB / 2; h >= 1; h >>= 1)
 #pragma unroll
         for (int i = 0; i < h; ++i) ts[i] = ts[2 * i] + ts[2 * i + 1];
-      const float rs = row_sum4(ts[0]);
-      l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha[nb], rs);
+      l_sum[nb] = __builtin_fmaf(l_sum[nb], alpha[nb], ts[0]);
       if constexpr (kRescale) {
         if (__any(rebase)) {  // acc * 1 == acc for the lanes that keep their reference
 #pragma unroll
@@ -1136,7 +1139,7 @@ __global__ __launch_bounds__(64 * waves_for(D), 1) void prefill_kernel(PrefillAr
       if (t + 1 < n_tiles) spec_iter(t + 1, s1, s);
     }
     if (o_rows) take_p(n_tiles - 1);
-    // l and m of the rows to wave 4, which writes the outputs
+    // l (lane shares) and m of the rows to wave 4, which writes the outputs
     float* xl = reinterpret_cast<float*>(xb + 2 * C::XSLOT);
     if (s_rows) {
       xl[lane] = l_sum[0];
