@@ -73,6 +73,9 @@ RANDOM_CASES = [
     (20, 8, 2, 512, 1, "bf16", [(150, 150), (151, 4)]),
     (21, 8, 2, 512, 12, "fp8_e4m3", [(130, 130), (131, 1), (4097, 2)]),
     (22, 8, 8, 512, 64, "bf16", [(180, 180), (181, 35), (7, 7)]),
+    # a 96-wide group: a wave's 32 packed rows span two tokens' heads (the kernels split packed
+    # rows into token and q head by a multiply-shift)
+    (23, 96, 1, 128, 16, "bf16", [(90, 90), (91, 3), (33, 1)]),
 ]
 
 
