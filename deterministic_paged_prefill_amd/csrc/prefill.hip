@@ -165,11 +165,6 @@ __device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-// Butterfly over the four lanes (l, l^16, l^32, l^48) holding one query row, on the gfx950
-// lane-swap instructions: permlane16_swap(x, x) hands every lane the pair {x[l & ~16],
-// x[l | 16]} and permlane32_swap(x, x) the pair {x[l & 31], x[(l & 31) + 32]}, always in that
-// order, so each lane of a row combines the same operands in the same order and ends with the
-// same bits: ((x0 + x1) + (x2 + x3)) for the sum.
 // Maximum of two scores (never NaN) as one instruction: fmaxf would first quiet each operand
 // it cannot prove canonical (max(x, x)), which is every value from a lane swap.
 __device__ inline float max2(float a, float b) {
@@ -177,6 +172,12 @@ __device__ inline float max2(float a, float b) {
   asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
+
+// Butterfly over the four lanes (l, l^16, l^32, l^48) holding one query row, on the gfx950
+// lane-swap instructions: permlane16_swap(x, x) hands every lane the pair {x[l & ~16],
+// x[l | 16]} and permlane32_swap(x, x) the pair {x[l & 31], x[(l & 31) + 32]}, always in that
+// order, so each lane of a row combines the same operands in the same order and ends with the
+// same bits: ((x0 + x1) + (x2 + x3)) for the sum.
 __device__ inline float row_max4(float x) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   x = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
