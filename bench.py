@@ -329,7 +329,7 @@ def main() -> int:
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-others", action="store_true")
-    ap.add_argument("--only", choices=["extend", "prefill", "decode", "copy", "stream"], default=None,
+    ap.add_argument("--only", choices=["extend", "prefill", "decode", "copy", "stream", "mixed", "fp8_8k"], default=None,
                     help="run one leg only and print its timing (for profiler runs)")
     args = ap.parse_args()
 
@@ -446,6 +446,20 @@ def main() -> int:
         del pr
 
     # ---------------------------------------------------------------- long-KV decode
+    # ---------------------------------------------------------------- profiler runs of two other legs
+    if args.only in ("mixed", "fp8_8k"):  # only the timed launches of that leg
+        if args.only == "mixed":
+            w_o = wl.mixed_batch()
+            b_o = w_o.batches["mixed"]
+        else:
+            w_o = wl.long_fp8()
+            b_o = w_o.batches["prefill_8192"]
+        r_o = Runner(w_o, b_o, replicas=1)
+        ms_o, _ = r_o.timed(args.steps, args.warmup)
+        fl_o = causal_flops(b_o, w_o.num_qo_heads, w_o.head_dim)
+        log(f"{args.only}: {ms_o * 1e3:.2f} us/step, {fl_o / (ms_o * 1e-3) / 1e12:.1f} TFLOP/s causal")
+        return 0
+
     if args.only in (None, "decode") and not args.no_decode:
         log("building long-KV decode workload")
         work_d = wl.decode_batch(full_prompts=0)

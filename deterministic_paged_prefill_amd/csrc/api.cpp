@@ -208,7 +208,8 @@ dpp_status launch_passes(const dpp_plan* plan, const void* q, const void* k_pool
     m.merge_begin = plan->merge_pass[(size_t)p];
     m.num_merges = plan->merge_pass[(size_t)p + 1] - m.merge_begin;
     if (m.num_merges > 0) {
-      e = launch_merge(m, plan->cfg.head_dim, plan->cfg.num_kv_heads, stream);
+      const bool all_narrow = plan->item_narrow[(size_t)p] == plan->item_pass[(size_t)p];
+      e = launch_merge(m, plan->cfg.head_dim, plan->cfg.num_kv_heads, all_narrow ? kNarrowRows : m.block_m, stream);
       if (e != hipSuccess) return hip_fail(e, "merge launch");
     }
   }

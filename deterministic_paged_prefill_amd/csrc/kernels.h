@@ -15,7 +15,9 @@ hipError_t launch_prefill(const PrefillArgs& a, int head_dim, int kv_dtype, bool
                           hipStream_t stream);
 
 // Merge of the split partials of one pass: grid (num_merges, num_kv_heads).
-hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream);
+// max_tile_rows: the most rows a merged tile of the pass can have (a pass of narrow tiles has
+// at most kNarrowRows); it sizes how many workgroups share a tile's rows.
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, int max_tile_rows, hipStream_t stream);
 
 // Standalone merge over dense [rows, splits, heads, D] partials.
 hipError_t launch_merge_dense(const MergeDenseArgs& a, hipStream_t stream);

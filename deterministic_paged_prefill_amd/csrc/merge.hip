@@ -42,6 +42,39 @@ __device__ inline uint32_t pack_bf16x2(float lo, float hi) {
 constexpr int kBatch = 8;
 template <class LseAt, class OAt>
 __device__ inline f32x4 merge4(int S, LseAt lse2_at, OAt o_at, float* lse2_out) {
+  if (S <= kBatch) {
+    // every partial of the row in one round trip; then the same arithmetic as below
+    float l[kBatch];
+    f32x4 os[kBatch];
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      const bool in = u < S;
+      l[u] = in ? lse2_at(u) : -INFINITY;
+      os[u] = in ? o_at(u) : f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) M = fmaxf(M, l[u]);
+    if (M == -INFINITY) {
+      *lse2_out = -INFINITY;
+      return f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    f32x4 num = f32x4{0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll
+    for (int u = 0; u < kBatch; ++u) {
+      if (l[u] == -INFINITY) continue;
+      const float w = (l[u] == M) ? 1.f : __builtin_amdgcn_exp2f(l[u] - M);
+      num[0] = __builtin_fmaf(w, os[u][0], num[0]);
+      num[1] = __builtin_fmaf(w, os[u][1], num[1]);
+      num[2] = __builtin_fmaf(w, os[u][2], num[2]);
+      num[3] = __builtin_fmaf(w, os[u][3], num[3]);
+      den = den + w;
+    }
+    const float inv = 1.f / den;
+    *lse2_out = M + __builtin_amdgcn_logf(den);
+    return f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
+  }
   float M = -INFINITY;
   for (int s0 = 0; s0 < S; s0 += kBatch) {
     float l[kBatch];
@@ -81,7 +114,13 @@ __device__ inline f32x4 merge4(int S, LseAt lse2_at, OAt o_at, float* lse2_out) 
   return f32x4{num[0] * inv, num[1] * inv, num[2] * inv, num[3] * inv};
 }
 
-// Planned merge: grid (merges in pass, kv heads); each block merges one q tile's rows.
+// Planned merge: grid (merges in pass, kv heads, Z); block z merges passes z, z + Z, ... of
+// one q tile's rows (a pass: kMergeThreads / (D / 4) rows side by side), Z = the tile's
+// passes, at most kMergeRowSplit. A row's partials are read with one round trip per batch
+// of splits, so the launch needs many rows in flight to stream; the split of a tile's rows
+// over several blocks gives it that. Every row is still merged by one thread group in one
+// fixed order.
+constexpr int kMergeRowSplit = 8;
 template <int D>
 __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   constexpr int kTpr = D / 4;              // threads per row (4 columns each)
@@ -97,7 +136,8 @@ __global__ __launch_bounds__(kMergeThreads) void merge_kernel(MergeArgs a) {
   const int ctx = rq.kv_len - rq.qo_len;
   const int col = (threadIdx.x % kTpr) * 4;
   const int stride = slot_rows_for(tile_rows);
-  for (int lr = threadIdx.x / kTpr; lr < tile_rows; lr += kRowsPerPass) {
+  for (int lr = (int)blockIdx.z * kRowsPerPass + (int)threadIdx.x / kTpr; lr < tile_rows;
+       lr += kRowsPerPass * (int)gridDim.z) {
     const int R = mi.row_start + lr;
     const int token = R / g;
     const int p = ctx + token;
@@ -144,8 +184,11 @@ __global__ __launch_bounds__(kMergeThreads) void merge_dense_kernel(MergeDenseAr
 
 }  // namespace
 
-hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, hipStream_t stream) {
-  dim3 grid((unsigned)a.num_merges, (unsigned)num_kv_heads);
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int num_kv_heads, int max_tile_rows, hipStream_t stream) {
+  const int rows_per_pass = kMergeThreads / (head_dim / 4);
+  const int passes = (max_tile_rows + rows_per_pass - 1) / rows_per_pass;
+  const int z = passes < 1 ? 1 : (passes < kMergeRowSplit ? passes : kMergeRowSplit);
+  dim3 grid((unsigned)a.num_merges, (unsigned)num_kv_heads, (unsigned)z);
   if (head_dim == 64)
     hipLaunchKernelGGL(merge_kernel<64>, grid, dim3(kMergeThreads), 0, stream, a);
   else if (head_dim == 128)
